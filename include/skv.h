@@ -1,0 +1,218 @@
+/*
+ * skv.h - shared-prefix multi-LoRA attention over one paged context cache.
+ *
+ * Several LoRA agents share one backbone. The base K/V of a shared context is
+ * computed once with base weights and stored once; every agent attends over
+ * that shared prefix followed by its own suffix. Agent i's value for token j is
+ * V_base[j] + (X_j A_i) B_i, and the library applies it as
+ *     O = P V_base + (P V_lr) B_i,
+ * keeping only the rank-r rows V_lr = X A in the cache, so no agent's
+ * full-width adapter value cache is ever formed.
+ *
+ * Sources (web pages; cited by page and part):
+ *   LRAgent review (pith.science, arXiv 2602.01053), "What carries the
+ *     argument": the value decomposition Y_i = X W0 + (X A_i) B_i (the paper's
+ *     Eq. 3) and the reorder O = P V_base + (P V_lr) B, with B applied once
+ *     per query block (its Eq. 12); Figs. 2-3: BaseShared (one LR cache per
+ *     agent) and BaseLRShared (shared A, one LR cache).
+ *   paperlayer summary of arXiv 2609.17109, Sec. 2: prefix KV computed once
+ *     with adapters disabled, specialist takes over at a boundary b;
+ *     Sec. 3.2: a paged cache is the route to physically shared storage.
+ *   RoleKV write-up (devpost), "What it does" / "How we built it": one shared
+ *     KV cache, crop and recompute at a role handoff; "Challenges": pass the
+ *     adapter offsets explicitly or the adapter silently turns off.
+ *
+ * Conventions
+ *   - All tensors are bf16 (passed as uint16_t bit patterns), row-major and
+ *     contiguous, and live in DEVICE memory: k, v, x, A, B, q, o.
+ *   - Small integer arrays (agents, lengths, counts) live in HOST memory.
+ *   - Hq = n_q_heads, Hkv = n_kv_heads, G = Hq / Hkv, d = head_dim,
+ *     r = rank, N = n_agents. Query head h reads KV head floor(h / G).
+ *   - A sequence id is SKV_SHARED (-1) or an agent id 0..N-1. Agent i's view
+ *     at a layer is SHARED[0:b_i] followed by OWN_i[0:S_i]; b_i is the same on
+ *     every layer, S_i is per layer.
+ *   - Low-rank planes: BaseShared keeps one plane per agent (plane i holds
+ *     X A_i); BaseLRShared keeps plane 0 only (X A with the shared A). Agent
+ *     i's own rows always use plane_of(i) = (mode == BaseShared ? i : 0).
+ *   - Softmax scale is 1/sqrt(d). A query at view position t sees view
+ *     positions 0..t (decode appends the token, then attends).
+ *   - Every call validates on the host before it enqueues anything, and is
+ *     all-or-nothing: on error the cache state is unchanged. Device work is
+ *     enqueued on the stream given at create and no call waits for the GPU
+ *     (except skv_sync). Faults in device work surface at skv_sync.
+ *   - Ownership: the caller owns every device buffer and the arena, and keeps
+ *     them alive until the stream work that uses them has completed. The
+ *     library never allocates device memory; it carves its pools, page tables
+ *     and scratch out of the arena. Host metadata belongs to the library.
+ *     One host thread per context.
+ */
+#ifndef SKV_H
+#define SKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SKV_SHARED (-1)
+#define SKV_MAX_AGENTS 16
+
+enum skv_mode { SKV_BASE_SHARED = 0, SKV_BASE_LR_SHARED = 1 };
+
+enum skv_status {
+  SKV_OK = 0,
+  SKV_ERR_ARG = -1,         /* bad argument (range, null pointer, shape)            */
+  SKV_ERR_STATE = -2,       /* lengths disagree with the cache, LR rows missing,    */
+                            /* crop out of range                                    */
+  SKV_ERR_OOM = -3,         /* page pool of a layer exhausted                       */
+  SKV_ERR_UNSUPPORTED = -4, /* configuration the device code does not handle        */
+  SKV_ERR_HIP = -5          /* a HIP runtime call failed                            */
+};
+
+typedef uint16_t skv_bf16; /* bf16 bit pattern */
+
+typedef struct skv_config {
+  int32_t n_layers;
+  int32_t n_q_heads;   /* Hq, a multiple of n_kv_heads                                  */
+  int32_t n_kv_heads;  /* Hkv                                                            */
+  int32_t head_dim;    /* d: 64 or 128                                                   */
+  int32_t hidden;      /* width of X (input of A), a multiple of 64                      */
+  int32_t rank;        /* r: 4, 8, 16 or 32                                              */
+  int32_t n_agents;    /* N: 1..SKV_MAX_AGENTS                                           */
+  int32_t mode;        /* SKV_BASE_SHARED or SKV_BASE_LR_SHARED                          */
+  int32_t page_size;   /* rows per page, a power of two (the GPU build requires 64)     */
+  int32_t max_pages;   /* pages per layer in the pool (shared by all sequences)         */
+} skv_config;
+
+typedef struct skv_ctx skv_ctx;
+
+/* Bytes of device memory skv_create needs for cfg (0 if cfg is invalid). */
+size_t skv_arena_bytes(const skv_config* cfg);
+
+/* Create a context over a caller-owned device arena of at least
+ * skv_arena_bytes(cfg) bytes (256-byte aligned). stream is a hipStream_t
+ * (NULL = default stream). Errors: ARG (bad config, small arena),
+ * UNSUPPORTED (page_size or shape the device code does not handle). */
+int skv_create(const skv_config* cfg, void* dev_arena, size_t arena_bytes, void* stream,
+               skv_ctx** out);
+
+/* Free host metadata. Does not touch the arena. NULL is allowed. */
+void skv_destroy(skv_ctx* ctx);
+
+/* a1 / a3: append n rows of base-weight K and V to the end of sequence seq at
+ * one layer (LRAgent review Fig. 2: the base cache is computed once and
+ * shared; RoleKV "What it does": a role switch only computes the new tokens).
+ * k, v: device [n][Hkv][d]. New pages take the lowest free page ids of the
+ * layer. n == 0 is a no-op. Errors: ARG, OOM (nothing is appended). */
+int skv_append_base(skv_ctx* ctx, int layer, int seq, int n, const skv_bf16* k,
+                    const skv_bf16* v);
+
+/* a2: append n low-rank rows bf16(X A) (fp32 accumulation, round to nearest
+ * even) to plane `plane` of sequence seq at one layer, after the rows it
+ * already holds (LRAgent review, "What carries the argument": the adapter
+ * term is stored as the rank-r intermediate X A; Fig. 3: BaseShared fills it
+ * for every context token the agent has not processed, BaseLRShared once).
+ * x: device [n][hidden] or NULL for adapter-off zero rows (paperlayer Sec. 2:
+ * prefix computed with adapters disabled); A: device [hidden][r] (ignored
+ * when x is NULL). For SKV_SHARED, plane is 0..planes-1; for an agent, plane
+ * must be plane_of(agent). LR rows may not run ahead of base rows.
+ * Errors: ARG, STATE. */
+int skv_append_lowrank(skv_ctx* ctx, int layer, int seq, int plane, int n, const skv_bf16* x,
+                       const skv_bf16* A);
+
+/* a2 + a3 batched: for each listed agent, append counts[i] own rows of base
+ * K/V and their low-rank rows in one launch. agents/counts: host [n]. k, v:
+ * device [sum counts][Hkv][d]; x: device [sum counts][hidden] or NULL (zero LR
+ * rows); A: device [N][hidden][r] in BaseShared (A_i indexed by agent id) or
+ * [hidden][r] in BaseLRShared. Each agent's own LR rows must be level with its
+ * base rows before the call. Errors: ARG, STATE, OOM (nothing is appended). */
+int skv_append_agents(skv_ctx* ctx, int layer, int n, const int* agents, const int* counts,
+                      const skv_bf16* k, const skv_bf16* v, const skv_bf16* x,
+                      const skv_bf16* A);
+
+/* a4: suffix prefill attention at one layer. For each listed agent i (host
+ * arrays agents/base_len/suffix_len/n_q of length n), the queries are the last
+ * n_q[i] positions of its view, already appended. base_len[i] and
+ * suffix_len[i] must equal the cache's b_i and S_i at this layer (RoleKV
+ * "Challenges": offsets are passed explicitly and checked). Each query at
+ * view position t computes softmax(q K[0..t]^T / sqrt(d)) over the view and
+ * o = P V_base + (P V_lr) B_i[:, g*d:(g+1)*d] (LRAgent review, "What carries
+ * the argument"), with B_i applied once per query block.
+ * q, o: device [sum n_q][Hq][d] (agent blocks in call order). B: device
+ * [N][r][Hkv*d] indexed by agent id. Agents must be distinct.
+ * Errors: ARG, STATE (lengths differ, LR rows do not cover the view). */
+int skv_attn_prefill(skv_ctx* ctx, int layer, int n, const int* agents, const int* base_len,
+                     const int* suffix_len, const int* n_q, const skv_bf16* q,
+                     const skv_bf16* B, skv_bf16* o);
+
+/* a5 + a6: decode attention, one query per listed agent at the last position
+ * of its view: the same result as skv_attn_prefill with n_q[i] = 1. The
+ * shared prefix is streamed from HBM once per KV head for all listed agents'
+ * query rows, split over the GPU, and the partial softmax states are merged
+ * before B_i is applied. q, o: device [n][Hq][d]. Errors: as prefill. */
+int skv_attn_decode(skv_ctx* ctx, int layer, int n, const int* agents, const int* base_len,
+                    const int* suffix_len, const skv_bf16* q, const skv_bf16* B, skv_bf16* o);
+
+/* a7: set a view length on every layer (RoleKV "How we built it": crop at a
+ * handoff; paperlayer Sec. 2: takeover boundary). Host metadata only.
+ *   seq = agent i with no own rows and new_len >= b_i: (re)attach, b_i = new_len
+ *         (new_len <= shared length on every layer).
+ *   seq = agent i, b_i <= new_len <= b_i + min_l S_i: own rows truncated.
+ *   seq = agent i, new_len < b_i: own rows dropped, b_i = new_len.
+ *   seq = SKV_SHARED: max_i b_i <= new_len <= shared length on every layer.
+ * Pages lying wholly beyond a new length are freed. Freed pages keep their
+ * bytes. Errors: ARG, STATE. */
+int skv_crop(skv_ctx* ctx, int seq, int new_len);
+
+/* Lengths at one layer. Any output pointer may be NULL. base_len, suffix_len,
+ * lr_own: host [N]; lr_shared: host [planes]. P receives the shared length. */
+int skv_get_lens(const skv_ctx* ctx, int layer, int* P, int* base_len, int* suffix_len,
+                 int* lr_shared, int* lr_own);
+
+/* Page ids of seq at layer, in order, into host ids[cap]. Returns the count
+ * (which may exceed cap) or a negative error. */
+int skv_get_pages(const skv_ctx* ctx, int layer, int seq, int32_t* ids, int cap);
+
+/* Device pool layout, for byte-level inspection:
+ *   K  [layer][page][Hkv][page_size][d]        bf16
+ *   VT [layer][page][Hkv][d][page_size]        bf16 (V stored transposed)
+ *   LRT[plane][layer][page][r][page_size]      bf16 (low-rank rows transposed)
+ *   tables [layer][1 + N][max_pages]           int32 (slot 0 = SHARED)
+ * Offsets are in bytes from the arena start. */
+typedef struct skv_pools {
+  uint64_t k_off, vt_off, lrt_off, tables_off, scratch_off, scratch_bytes, arena_bytes;
+  int32_t planes;
+} skv_pools;
+int skv_get_pools(const skv_ctx* ctx, skv_pools* out);
+
+/* Token accounting (RoleKV "Challenges": honest cost accounting). */
+typedef struct skv_counters {
+  int64_t base_rows_shared, base_rows_own, lr_rows, lr_zero_rows, rows_cropped;
+  int64_t pages_alloc, pages_freed, launches;
+} skv_counters;
+int skv_get_counters(const skv_ctx* ctx, skv_counters* out);
+
+/* Kernel timing with HIP events recorded on the context stream around each
+ * launch, while enabled. Kinds: 0 append K/V, 1 append low-rank, 2 decode
+ * attention (split pass), 3 decode merge + B, 4 prefill attention. */
+#define SKV_KERNEL_KINDS 5
+typedef struct skv_kernel_times {
+  double ms[SKV_KERNEL_KINDS];
+  int64_t launches[SKV_KERNEL_KINDS];
+} skv_kernel_times;
+int skv_set_timing(skv_ctx* ctx, int enable);
+/* Waits for the stream, sums the recorded intervals, and clears them. */
+int skv_collect_timing(skv_ctx* ctx, skv_kernel_times* out);
+
+/* Wait for all work enqueued by this context. Errors: HIP. */
+int skv_sync(skv_ctx* ctx);
+
+/* Message of the last failed call on ctx ("" if none). */
+const char* skv_last_error(const skv_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SKV_H */

@@ -1,0 +1,36 @@
+// Null device backend: accepts every job and touches no memory. Linked into
+// libskv_host.so, a CPU-only build of the host runtime used to test lengths,
+// page tables, crop and validation on machines without a GPU. It is never
+// part of libskv.so, the GPU library.
+#include "backend.h"
+
+namespace skv {
+
+int dev_check(const Geometry&) { return SKV_OK; }
+uint64_t dev_scratch_bytes(const Geometry&) { return 0; }
+int dev_init(Geometry& g) {
+  g.dev = nullptr;
+  return SKV_OK;
+}
+void dev_fini(Geometry&) {}
+int dev_append(const Geometry& g, const AppendJob&) {
+  ++*g.launches;
+  return SKV_OK;
+}
+int dev_attn_decode(const Geometry& g, const AttnJob&) {
+  ++*g.launches;
+  return SKV_OK;
+}
+int dev_attn_prefill(const Geometry& g, const AttnJob&) {
+  ++*g.launches;
+  return SKV_OK;
+}
+int dev_sync(const Geometry&) { return SKV_OK; }
+int dev_set_timing(Geometry&, bool) { return SKV_OK; }
+int dev_collect_timing(Geometry&, skv_kernel_times* out) {
+  *out = skv_kernel_times{};
+  return SKV_OK;
+}
+const char* dev_last_error() { return ""; }
+
+}  // namespace skv

@@ -1,0 +1,557 @@
+// Host runtime of the shared-prefix multi-LoRA attention library: the C ABI
+// declared in include/skv.h. It validates every call, owns the metadata of
+// the paged store (lengths, page tables, low-rank coverage, free pages), and
+// turns each call into backend jobs. It never allocates device memory and
+// never waits for the GPU except in skv_sync / skv_collect_timing.
+//
+// Store model (readings of the pages; see include/skv.h for the sources):
+//   one shared sequence per layer holds base-weight K/V computed once
+//   (LRAgent review Fig. 2; paperlayer summary of arXiv 2609.17109 Sec. 2),
+//   agent i's view is SHARED[0:b_i] ++ OWN_i[0:S_i], pages are page_size
+//   rows, a new page takes the lowest free id of its layer, and a crop frees
+//   the pages lying wholly beyond the new length (paperlayer Sec. 3.2: a
+//   paged cache is the route to physical sharing; RoleKV "How we built it":
+//   crop at a handoff).
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <set>
+#include <string>
+#include <vector>
+
+#include "backend.h"
+
+namespace {
+
+using skv::AppendJob;
+using skv::AttnJob;
+using skv::Geometry;
+using skv::Span;
+
+struct Layer {
+  std::set<int32_t> free;                   // free page ids; *begin() is the lowest
+  std::vector<std::vector<int32_t>> tbl;    // [1 + N] page ids per sequence slot
+  std::vector<int> len;                     // [1 + N] rows per sequence slot
+  std::vector<int> lr_shared;               // [planes] low-rank rows over the shared sequence
+  std::vector<int> lr_own;                  // [N] low-rank rows over each agent's own rows
+};
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+bool valid_config(const skv_config* c) {
+  if (!c) return false;
+  auto pow2 = [](int x) { return x > 0 && (x & (x - 1)) == 0; };
+  return c->n_layers >= 1 && c->n_kv_heads >= 1 && c->n_q_heads >= c->n_kv_heads &&
+         c->n_q_heads % c->n_kv_heads == 0 && (c->head_dim == 64 || c->head_dim == 128) &&
+         (c->rank == 4 || c->rank == 8 || c->rank == 16 || c->rank == 32) && c->n_agents >= 1 &&
+         c->n_agents <= SKV_MAX_AGENTS &&
+         (c->mode == SKV_BASE_SHARED || c->mode == SKV_BASE_LR_SHARED) && c->hidden >= 64 &&
+         c->hidden % 64 == 0 && pow2(c->page_size) && c->page_size >= 4 &&
+         c->page_size <= 1024 && c->max_pages >= 1;
+}
+
+Geometry geometry_of(const skv_config* c) {
+  Geometry g{};
+  g.L = c->n_layers;
+  g.Hq = c->n_q_heads;
+  g.Hkv = c->n_kv_heads;
+  g.G = c->n_q_heads / c->n_kv_heads;
+  g.D = c->head_dim;
+  g.hidden = c->hidden;
+  g.r = c->rank;
+  g.N = c->n_agents;
+  g.mode = c->mode;
+  g.ps = c->page_size;
+  g.max_pages = c->max_pages;
+  g.planes = c->mode == SKV_BASE_SHARED ? c->n_agents : 1;
+  uint64_t off = 0;
+  g.k_off = off;
+  off = align256(off + 2 * (uint64_t)g.L * g.k_layer());
+  g.vt_off = off;
+  off = align256(off + 2 * (uint64_t)g.L * g.k_layer());
+  g.lrt_off = off;
+  off = align256(off + 2 * (uint64_t)g.planes * g.lr_plane());
+  g.tbl_off = off;
+  off = align256(off + 4 * (uint64_t)g.L * g.tbl_layer());
+  g.scratch_off = off;
+  g.scratch_bytes = align256(skv::dev_scratch_bytes(g));
+  off += g.scratch_bytes;
+  g.arena_bytes = off;
+  return g;
+}
+
+}  // namespace
+
+struct skv_ctx {
+  Geometry g{};
+  std::vector<Layer> layers;
+  std::vector<int> base_len;
+  skv_counters counters{};
+  std::string err;
+
+  int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    err = buf;
+    return code;
+  }
+  int plane_of(int agent) const { return g.mode == SKV_BASE_SHARED ? agent : 0; }
+  static int slot_of(int seq) { return seq + 1; }  // SHARED -> 0, agent a -> 1 + a
+  bool seq_ok(int seq) const { return seq == SKV_SHARED || (seq >= 0 && seq < g.N); }
+  int min_len(int slot) const {
+    int m = layers[0].len[slot];
+    for (auto& l : layers) m = std::min(m, l.len[slot]);
+    return m;
+  }
+  int max_base() const {
+    int m = 0;
+    for (int b : base_len) m = std::max(m, b);
+    return m;
+  }
+  // Release pages of (layer, slot) whose index is >= ceil(new_len / ps).
+  void free_beyond(Layer& l, int slot, int new_len) {
+    size_t keep = (size_t)ceil_div(new_len, g.ps);
+    auto& t = l.tbl[slot];
+    for (size_t i = keep; i < t.size(); ++i) {
+      l.free.insert(t[i]);
+      counters.pages_freed++;
+    }
+    if (t.size() > keep) t.resize(keep);
+  }
+};
+
+namespace {
+
+// Split rows [pos0, pos0 + n) of a sequence into spans that fit the job limits
+// and append them to jobs (opening new jobs when a job is full).
+void add_spans(const skv_ctx* c, std::vector<AppendJob>& jobs, const AppendJob& proto,
+               const std::vector<int32_t>& table, int slot, int pos0, int n, int src_row,
+               int plane, const uint16_t* a) {
+  const int ps = c->g.ps;
+  int done = 0;
+  while (done < n) {
+    if (jobs.empty() || jobs.back().n_spans == skv::kMaxJobSpans ||
+        jobs.back().n_ids == skv::kMaxJobPages) {
+      jobs.push_back(proto);
+    }
+    AppendJob& j = jobs.back();
+    int p = pos0 + done;
+    int first_page = p / ps;
+    int room = skv::kMaxJobPages - j.n_ids;
+    // rows until the end of the last page that still fits in this job
+    int last_row_excl = (first_page + room) * ps;
+    int take = std::min(n - done, last_row_excl - p);
+    int n_pages = ceil_div(p + take, ps) - first_page;
+    Span s{};
+    s.seq_slot = slot;
+    s.pos0 = p;
+    s.n = take;
+    s.src_row = src_row + done;
+    s.first_page = first_page;
+    s.n_pages = n_pages;
+    s.ids_off = j.n_ids;
+    s.plane = plane;
+    s.a = a;
+    for (int i = 0; i < n_pages; ++i) j.ids[j.n_ids++] = table[first_page + i];
+    j.spans[j.n_spans++] = s;
+    done += take;
+  }
+}
+
+int run_jobs(skv_ctx* c, const std::vector<AppendJob>& jobs) {
+  for (auto& j : jobs) {
+    int rc = skv::dev_append(c->g, j);
+    if (rc != SKV_OK) return c->fail(rc, "device append failed: %s", skv::dev_last_error());
+  }
+  return SKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t skv_arena_bytes(const skv_config* cfg) {
+  if (!valid_config(cfg)) return 0;
+  return (size_t)geometry_of(cfg).arena_bytes;
+}
+
+int skv_create(const skv_config* cfg, void* dev_arena, size_t arena_bytes, void* stream,
+               skv_ctx** out) {
+  if (!out) return SKV_ERR_ARG;
+  *out = nullptr;
+  if (!valid_config(cfg) || !dev_arena || ((uintptr_t)dev_arena & 255)) return SKV_ERR_ARG;
+  Geometry g = geometry_of(cfg);
+  if (arena_bytes < g.arena_bytes) return SKV_ERR_ARG;
+  int rc = skv::dev_check(g);
+  if (rc != SKV_OK) return rc;
+  auto* c = new skv_ctx();
+  c->g = g;
+  c->g.arena = (char*)dev_arena;
+  c->g.stream = stream;
+  c->g.launches = &c->counters.launches;
+  rc = skv::dev_init(c->g);
+  if (rc != SKV_OK) {
+    delete c;
+    return rc;
+  }
+  c->layers.resize(g.L);
+  for (auto& l : c->layers) {
+    for (int p = 0; p < g.max_pages; ++p) l.free.insert(l.free.end(), p);
+    l.tbl.assign(g.N + 1, {});
+    l.len.assign(g.N + 1, 0);
+    l.lr_shared.assign(g.planes, 0);
+    l.lr_own.assign(g.N, 0);
+  }
+  c->base_len.assign(g.N, 0);
+  *out = c;
+  return SKV_OK;
+}
+
+void skv_destroy(skv_ctx* c) {
+  if (!c) return;
+  skv::dev_fini(c->g);
+  delete c;
+}
+
+int skv_append_base(skv_ctx* c, int layer, int seq, int n, const skv_bf16* k, const skv_bf16* v) {
+  if (!c) return SKV_ERR_ARG;
+  if (layer < 0 || layer >= c->g.L) return c->fail(SKV_ERR_ARG, "layer %d out of range", layer);
+  if (!c->seq_ok(seq)) return c->fail(SKV_ERR_ARG, "sequence %d out of range", seq);
+  if (n < 0) return c->fail(SKV_ERR_ARG, "negative row count");
+  if (n == 0) return SKV_OK;
+  if (!k || !v) return c->fail(SKV_ERR_ARG, "null k or v");
+  Layer& l = c->layers[layer];
+  const int slot = skv_ctx::slot_of(seq);
+  const int cur = l.len[slot];
+  const int need = ceil_div(cur + n, c->g.ps) - (int)l.tbl[slot].size();
+  if (need > (int)l.free.size())
+    return c->fail(SKV_ERR_OOM, "layer %d: %d pages needed, %d free", layer, need,
+                   (int)l.free.size());
+  std::vector<int32_t> table = l.tbl[slot];
+  std::vector<int32_t> taken;
+  for (int i = 0; i < need; ++i) {
+    int32_t p = *l.free.begin();
+    l.free.erase(l.free.begin());
+    table.push_back(p);
+    taken.push_back(p);
+  }
+  AppendJob proto{};
+  proto.layer = layer;
+  proto.do_kv = true;
+  proto.update_tables = true;
+  proto.k = k;
+  proto.v = v;
+  std::vector<AppendJob> jobs;
+  add_spans(c, jobs, proto, table, slot, cur, n, 0, 0, nullptr);
+  int rc = run_jobs(c, jobs);
+  if (rc != SKV_OK) {
+    for (int32_t p : taken) l.free.insert(p);
+    return rc;
+  }
+  l.tbl[slot] = std::move(table);
+  l.len[slot] = cur + n;
+  c->counters.pages_alloc += need;
+  (seq == SKV_SHARED ? c->counters.base_rows_shared : c->counters.base_rows_own) += n;
+  return SKV_OK;
+}
+
+int skv_append_lowrank(skv_ctx* c, int layer, int seq, int plane, int n, const skv_bf16* x,
+                       const skv_bf16* A) {
+  if (!c) return SKV_ERR_ARG;
+  if (layer < 0 || layer >= c->g.L) return c->fail(SKV_ERR_ARG, "layer %d out of range", layer);
+  if (!c->seq_ok(seq)) return c->fail(SKV_ERR_ARG, "sequence %d out of range", seq);
+  if (seq == SKV_SHARED) {
+    if (plane < 0 || plane >= c->g.planes) return c->fail(SKV_ERR_ARG, "plane %d", plane);
+  } else if (plane != c->plane_of(seq)) {
+    return c->fail(SKV_ERR_ARG, "agent %d writes plane %d, not %d", seq, c->plane_of(seq), plane);
+  }
+  if (n < 0) return c->fail(SKV_ERR_ARG, "negative row count");
+  if (x && !A) return c->fail(SKV_ERR_ARG, "x given without A");
+  if (n == 0) return SKV_OK;
+  Layer& l = c->layers[layer];
+  const int slot = skv_ctx::slot_of(seq);
+  int& cov = seq == SKV_SHARED ? l.lr_shared[plane] : l.lr_own[seq];
+  if (cov + n > l.len[slot])
+    return c->fail(SKV_ERR_STATE, "low-rank rows %d..%d run ahead of %d base rows", cov, cov + n,
+                   l.len[slot]);
+  AppendJob proto{};
+  proto.layer = layer;
+  proto.do_lr = true;
+  proto.x = x;
+  std::vector<AppendJob> jobs;
+  add_spans(c, jobs, proto, l.tbl[slot], slot, cov, n, 0, plane, A);
+  int rc = run_jobs(c, jobs);
+  if (rc != SKV_OK) return rc;
+  cov += n;
+  (x ? c->counters.lr_rows : c->counters.lr_zero_rows) += n;
+  return SKV_OK;
+}
+
+int skv_append_agents(skv_ctx* c, int layer, int n, const int* agents, const int* counts,
+                      const skv_bf16* k, const skv_bf16* v, const skv_bf16* x,
+                      const skv_bf16* A) {
+  if (!c) return SKV_ERR_ARG;
+  const Geometry& g = c->g;
+  if (layer < 0 || layer >= g.L) return c->fail(SKV_ERR_ARG, "layer %d out of range", layer);
+  if (n < 0 || n > g.N) return c->fail(SKV_ERR_ARG, "agent count %d", n);
+  if (n == 0) return SKV_OK;
+  if (!agents || !counts) return c->fail(SKV_ERR_ARG, "null agents or counts");
+  if (x && !A) return c->fail(SKV_ERR_ARG, "x given without A");
+  std::vector<bool> seen(g.N, false);
+  long total = 0;
+  for (int i = 0; i < n; ++i) {
+    int a = agents[i];
+    if (a >= 0 && a < g.N && seen[a]) return c->fail(SKV_ERR_ARG, "duplicate agent %d", a);
+    if (a >= 0 && a < g.N) seen[a] = true;
+  }
+  for (int i = 0; i < n; ++i) {
+    int a = agents[i];
+    if (a < 0 || a >= g.N || counts[i] < 0)
+      return c->fail(SKV_ERR_ARG, "agent list entry %d (count %d)", a, counts[i]);
+    total += counts[i];
+  }
+  if (total == 0) return SKV_OK;
+  if (!k || !v) return c->fail(SKV_ERR_ARG, "null k or v");
+  Layer& l = c->layers[layer];
+  for (int i = 0; i < n; ++i) {
+    int slot = 1 + agents[i];
+    if (l.lr_own[agents[i]] != l.len[slot])
+      return c->fail(SKV_ERR_STATE, "agent %d low-rank rows (%d) lag base rows (%d)", agents[i],
+                     l.lr_own[agents[i]], l.len[slot]);
+  }
+  int need = 0;
+  for (int i = 0; i < n; ++i) {
+    int slot = 1 + agents[i];
+    need += ceil_div(l.len[slot] + counts[i], g.ps) - (int)l.tbl[slot].size();
+  }
+  if (need > (int)l.free.size())
+    return c->fail(SKV_ERR_OOM, "layer %d: %d pages needed, %d free", layer, need,
+                   (int)l.free.size());
+  std::vector<std::vector<int32_t>> tables(n);
+  std::vector<int32_t> taken;
+  for (int i = 0; i < n; ++i) {
+    int slot = 1 + agents[i];
+    tables[i] = l.tbl[slot];
+    int want = ceil_div(l.len[slot] + counts[i], g.ps) - (int)tables[i].size();
+    for (int p = 0; p < want; ++p) {
+      int32_t id = *l.free.begin();
+      l.free.erase(l.free.begin());
+      tables[i].push_back(id);
+      taken.push_back(id);
+    }
+  }
+  AppendJob proto{};
+  proto.layer = layer;
+  proto.do_kv = true;
+  proto.do_lr = true;
+  proto.update_tables = true;
+  proto.k = k;
+  proto.v = v;
+  proto.x = x;
+  std::vector<AppendJob> jobs;
+  const uint64_t a_stride = (uint64_t)g.hidden * g.r;
+  int row = 0;
+  for (int i = 0; i < n; ++i) {
+    int a = agents[i];
+    const uint16_t* ap = nullptr;
+    if (x) ap = g.mode == SKV_BASE_SHARED ? A + a_stride * a : A;
+    add_spans(c, jobs, proto, tables[i], 1 + a, l.len[1 + a], counts[i], row, c->plane_of(a), ap);
+    row += counts[i];
+  }
+  int rc = run_jobs(c, jobs);
+  if (rc != SKV_OK) {
+    for (int32_t p : taken) l.free.insert(p);
+    return rc;
+  }
+  for (int i = 0; i < n; ++i) {
+    int slot = 1 + agents[i];
+    l.tbl[slot] = std::move(tables[i]);
+    l.len[slot] += counts[i];
+    l.lr_own[agents[i]] += counts[i];
+  }
+  c->counters.pages_alloc += need;
+  c->counters.base_rows_own += total;
+  (x ? c->counters.lr_rows : c->counters.lr_zero_rows) += total;
+  return SKV_OK;
+}
+
+static int validate_attend(skv_ctx* c, int layer, int n, const int* agents, const int* base_len,
+                           const int* suffix_len, const int* n_q, const void* q, const void* B,
+                           const void* o, AttnJob& job) {
+  const Geometry& g = c->g;
+  if (layer < 0 || layer >= g.L) return c->fail(SKV_ERR_ARG, "layer %d out of range", layer);
+  if (n < 1 || n > g.N) return c->fail(SKV_ERR_ARG, "agent count %d", n);
+  if (!agents || !base_len || !suffix_len || !q || !B || !o)
+    return c->fail(SKV_ERR_ARG, "null argument");
+  const Layer& l = c->layers[layer];
+  std::vector<bool> seen(g.N, false);
+  for (int i = 0; i < n; ++i) {
+    int a = agents[i];
+    if (a >= 0 && a < g.N && seen[a]) return c->fail(SKV_ERR_ARG, "duplicate agent %d", a);
+    if (a >= 0 && a < g.N) seen[a] = true;
+  }
+  job = AttnJob{};
+  job.layer = layer;
+  job.n = n;
+  int row = 0;
+  for (int i = 0; i < n; ++i) {
+    int a = agents[i];
+    if (a < 0 || a >= g.N) return c->fail(SKV_ERR_ARG, "agent id %d", a);
+    int b = c->base_len[a], S = l.len[1 + a];
+    if (base_len[i] != b || suffix_len[i] != S)
+      return c->fail(SKV_ERR_STATE,
+                     "agent %d: caller lengths (b=%d, S=%d) differ from the cache (b=%d, S=%d)", a,
+                     base_len[i], suffix_len[i], b, S);
+    int nq = n_q ? n_q[i] : 1;
+    if (b + S < 1 || nq < 1 || nq > b + S)
+      return c->fail(SKV_ERR_ARG, "agent %d: %d queries over a view of %d", a, nq, b + S);
+    int p = c->plane_of(a);
+    if (l.lr_shared[p] < b || l.lr_own[a] < S)
+      return c->fail(SKV_ERR_STATE, "agent %d: low-rank rows do not cover the view", a);
+    job.ag[i] = skv::AttnAgent{a, b, S, p, nq, row};
+    row += nq;
+  }
+  job.q = (const uint16_t*)q;
+  job.B = (const uint16_t*)B;
+  job.o = (uint16_t*)o;
+  return SKV_OK;
+}
+
+int skv_attn_prefill(skv_ctx* c, int layer, int n, const int* agents, const int* base_len,
+                     const int* suffix_len, const int* n_q, const skv_bf16* q, const skv_bf16* B,
+                     skv_bf16* o) {
+  if (!c) return SKV_ERR_ARG;
+  if (!n_q) return c->fail(SKV_ERR_ARG, "null n_q");
+  AttnJob job;
+  int rc = validate_attend(c, layer, n, agents, base_len, suffix_len, n_q, q, B, o, job);
+  if (rc != SKV_OK) return rc;
+  rc = skv::dev_attn_prefill(c->g, job);
+  if (rc != SKV_OK) return c->fail(rc, "device prefill failed: %s", skv::dev_last_error());
+  return SKV_OK;
+}
+
+int skv_attn_decode(skv_ctx* c, int layer, int n, const int* agents, const int* base_len,
+                    const int* suffix_len, const skv_bf16* q, const skv_bf16* B, skv_bf16* o) {
+  if (!c) return SKV_ERR_ARG;
+  AttnJob job;
+  int rc = validate_attend(c, layer, n, agents, base_len, suffix_len, nullptr, q, B, o, job);
+  if (rc != SKV_OK) return rc;
+  rc = skv::dev_attn_decode(c->g, job);
+  if (rc != SKV_OK) return c->fail(rc, "device decode failed: %s", skv::dev_last_error());
+  return SKV_OK;
+}
+
+int skv_crop(skv_ctx* c, int seq, int new_len) {
+  if (!c) return SKV_ERR_ARG;
+  if (!c->seq_ok(seq)) return c->fail(SKV_ERR_ARG, "sequence %d out of range", seq);
+  if (new_len < 0) return c->fail(SKV_ERR_ARG, "negative length");
+  const int shared_min = c->min_len(0);
+  if (seq == SKV_SHARED) {
+    if (new_len < c->max_base() || new_len > shared_min)
+      return c->fail(SKV_ERR_STATE, "shared crop to %d outside [%d, %d]", new_len, c->max_base(),
+                     shared_min);
+    for (auto& l : c->layers) {
+      c->counters.rows_cropped += l.len[0] - new_len;
+      l.len[0] = new_len;
+      for (auto& cov : l.lr_shared) cov = std::min(cov, new_len);
+      c->free_beyond(l, 0, new_len);
+    }
+    return SKV_OK;
+  }
+  const int slot = skv_ctx::slot_of(seq);
+  int& b = c->base_len[seq];
+  bool no_own = true;
+  for (auto& l : c->layers) no_own = no_own && l.len[slot] == 0;
+  if (no_own && new_len >= b) {
+    if (new_len > shared_min)
+      return c->fail(SKV_ERR_STATE, "attach at %d beyond shared length %d", new_len, shared_min);
+    b = new_len;
+    return SKV_OK;
+  }
+  int own;
+  if (new_len < b) {
+    own = 0;
+  } else {
+    own = new_len - b;
+    if (own > c->min_len(slot))
+      return c->fail(SKV_ERR_STATE, "crop to %d beyond the view (b=%d, min S=%d)", new_len, b,
+                     c->min_len(slot));
+  }
+  for (auto& l : c->layers) {
+    c->counters.rows_cropped += l.len[slot] - own;
+    l.len[slot] = own;
+    l.lr_own[seq] = std::min(l.lr_own[seq], own);
+    c->free_beyond(l, slot, own);
+  }
+  if (new_len < b) b = new_len;
+  return SKV_OK;
+}
+
+int skv_get_lens(const skv_ctx* c, int layer, int* P, int* base_len, int* suffix_len,
+                 int* lr_shared, int* lr_own) {
+  if (!c || layer < 0 || layer >= c->g.L) return SKV_ERR_ARG;
+  const Layer& l = c->layers[layer];
+  if (P) *P = l.len[0];
+  for (int a = 0; a < c->g.N; ++a) {
+    if (base_len) base_len[a] = c->base_len[a];
+    if (suffix_len) suffix_len[a] = l.len[1 + a];
+    if (lr_own) lr_own[a] = l.lr_own[a];
+  }
+  if (lr_shared)
+    for (int p = 0; p < c->g.planes; ++p) lr_shared[p] = l.lr_shared[p];
+  return SKV_OK;
+}
+
+int skv_get_pages(const skv_ctx* c, int layer, int seq, int32_t* ids, int cap) {
+  if (!c || layer < 0 || layer >= c->g.L || !c->seq_ok(seq) || cap < 0) return SKV_ERR_ARG;
+  const auto& t = c->layers[layer].tbl[skv_ctx::slot_of(seq)];
+  for (int i = 0; i < (int)t.size() && i < cap; ++i) ids[i] = t[i];
+  return (int)t.size();
+}
+
+int skv_get_pools(const skv_ctx* c, skv_pools* out) {
+  if (!c || !out) return SKV_ERR_ARG;
+  out->k_off = c->g.k_off;
+  out->vt_off = c->g.vt_off;
+  out->lrt_off = c->g.lrt_off;
+  out->tables_off = c->g.tbl_off;
+  out->scratch_off = c->g.scratch_off;
+  out->scratch_bytes = c->g.scratch_bytes;
+  out->arena_bytes = c->g.arena_bytes;
+  out->planes = c->g.planes;
+  return SKV_OK;
+}
+
+int skv_get_counters(const skv_ctx* c, skv_counters* out) {
+  if (!c || !out) return SKV_ERR_ARG;
+  *out = c->counters;
+  return SKV_OK;
+}
+
+int skv_set_timing(skv_ctx* c, int enable) {
+  if (!c) return SKV_ERR_ARG;
+  return skv::dev_set_timing(c->g, enable != 0);
+}
+
+int skv_collect_timing(skv_ctx* c, skv_kernel_times* out) {
+  if (!c || !out) return SKV_ERR_ARG;
+  int rc = skv::dev_collect_timing(c->g, out);
+  if (rc != SKV_OK) return c->fail(rc, "timing: %s", skv::dev_last_error());
+  return SKV_OK;
+}
+
+int skv_sync(skv_ctx* c) {
+  if (!c) return SKV_ERR_ARG;
+  int rc = skv::dev_sync(c->g);
+  if (rc != SKV_OK) return c->fail(rc, "sync: %s", skv::dev_last_error());
+  return SKV_OK;
+}
+
+const char* skv_last_error(const skv_ctx* c) { return c ? c->err.c_str() : "null context"; }
+
+}  // extern "C"

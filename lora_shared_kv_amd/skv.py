@@ -1,0 +1,290 @@
+"""Thin ctypes binding of the C ABI in include/skv.h (argument marshalling only).
+
+Every function has the name of the C entry point it wraps. Device tensors are
+torch tensors on the GPU (bf16, contiguous); their data pointers go straight
+to the library, which enqueues the work on the context's stream. Nothing here
+computes any part of the method, and there is no fallback: if the native
+library is missing, loading fails with an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+
+SKV_SHARED = -1
+SKV_BASE_SHARED = 0
+SKV_BASE_LR_SHARED = 1
+SKV_MAX_AGENTS = 16
+KERNEL_KINDS = ("append_kv", "append_lowrank", "decode_split", "decode_merge", "prefill")
+
+_CODES = {0: "OK", -1: "ARG", -2: "STATE", -3: "OOM", -4: "UNSUPPORTED", -5: "HIP"}
+
+_I = ctypes.c_int
+_P = ctypes.c_void_p
+_IP = ctypes.POINTER(ctypes.c_int)
+
+
+class skv_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_layers", "n_q_heads", "n_kv_heads", "head_dim", "hidden", "rank", "n_agents", "mode",
+        "page_size", "max_pages")]
+
+
+class skv_pools(ctypes.Structure):
+    _fields_ = [("k_off", ctypes.c_uint64), ("vt_off", ctypes.c_uint64), ("lrt_off", ctypes.c_uint64),
+                ("tables_off", ctypes.c_uint64), ("scratch_off", ctypes.c_uint64),
+                ("scratch_bytes", ctypes.c_uint64), ("arena_bytes", ctypes.c_uint64),
+                ("planes", ctypes.c_int32)]
+
+
+class skv_counters(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "base_rows_shared", "base_rows_own", "lr_rows", "lr_zero_rows", "rows_cropped",
+        "pages_alloc", "pages_freed", "launches")]
+
+
+class skv_kernel_times(ctypes.Structure):
+    _fields_ = [("ms", ctypes.c_double * 5), ("launches", ctypes.c_int64 * 5)]
+
+
+EXPORTS = {
+    "skv_arena_bytes": (ctypes.c_size_t, [ctypes.POINTER(skv_config)]),
+    "skv_create": (_I, [ctypes.POINTER(skv_config), _P, ctypes.c_size_t, _P, ctypes.POINTER(_P)]),
+    "skv_destroy": (None, [_P]),
+    "skv_append_base": (_I, [_P, _I, _I, _I, _P, _P]),
+    "skv_append_lowrank": (_I, [_P, _I, _I, _I, _I, _P, _P]),
+    "skv_append_agents": (_I, [_P, _I, _I, _IP, _IP, _P, _P, _P, _P]),
+    "skv_attn_prefill": (_I, [_P, _I, _I, _IP, _IP, _IP, _IP, _P, _P, _P]),
+    "skv_attn_decode": (_I, [_P, _I, _I, _IP, _IP, _IP, _P, _P, _P]),
+    "skv_crop": (_I, [_P, _I, _I]),
+    "skv_get_lens": (_I, [_P, _I, _IP, _IP, _IP, _IP, _IP]),
+    "skv_get_pages": (_I, [_P, _I, _I, ctypes.POINTER(ctypes.c_int32), _I]),
+    "skv_get_pools": (_I, [_P, ctypes.POINTER(skv_pools)]),
+    "skv_get_counters": (_I, [_P, ctypes.POINTER(skv_counters)]),
+    "skv_set_timing": (_I, [_P, _I]),
+    "skv_collect_timing": (_I, [_P, ctypes.POINTER(skv_kernel_times)]),
+    "skv_sync": (_I, [_P]),
+    "skv_last_error": (ctypes.c_char_p, [_P]),
+}
+
+_LIBS = {}
+
+
+def library_path(kind: str = "gpu") -> str:
+    return os.path.join(_PKG, "libskv.so" if kind == "gpu" else "libskv_host.so")
+
+
+def load_library(kind: str = "gpu"):
+    """kind="gpu": libskv.so (HIP kernels). kind="host": the null-device build for metadata tests."""
+    if kind in _LIBS:
+        return _LIBS[kind]
+    path = library_path(kind)
+    if not os.path.exists(path):
+        raise RuntimeError(f"native library {path} is not built; run `python -m lora_shared_kv_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in EXPORTS.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _LIBS[kind] = lib
+    return lib
+
+
+class SkvError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        self.code = _CODES.get(code, str(code))
+        super().__init__(f"skv error {self.code}: {msg}")
+
+
+def _ints(xs):
+    xs = [int(x) for x in xs]
+    return (ctypes.c_int * max(1, len(xs)))(*xs), len(xs)
+
+
+def _ptr(t, kind=None, shape=None, name="tensor"):
+    """Device pointer of a tensor (checked) or an int address; None -> NULL."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    import torch
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise TypeError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+class Ctx:
+    """An skv_ctx* with the library it came from and the arena it lives in."""
+
+    def __init__(self, lib, handle, cfg: dict, arena=None, kind="gpu"):
+        self.lib, self.handle, self.cfg, self.arena, self.kind = lib, handle, dict(cfg), arena, kind
+        c = self.cfg
+        self.G = c["n_q_heads"] // c["n_kv_heads"]
+        self.planes = c["n_agents"] if c["mode"] == SKV_BASE_SHARED else 1
+
+    def _check(self, rc):
+        if rc != 0:
+            raise SkvError(rc, self.lib.skv_last_error(self.handle).decode())
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            self.lib.skv_destroy(h)
+            self.handle = None
+
+
+def _cfg(cfg: dict) -> skv_config:
+    c = skv_config()
+    defaults = dict(page_size=64, mode=SKV_BASE_SHARED)
+    for name, _ in skv_config._fields_:
+        setattr(c, name, int(cfg.get(name, defaults.get(name, 0))))
+    return c
+
+
+def skv_arena_bytes(cfg: dict, kind: str = "gpu") -> int:
+    return int(load_library(kind).skv_arena_bytes(ctypes.byref(_cfg(cfg))))
+
+
+def skv_create(cfg: dict, arena, stream=None, kind: str = "gpu") -> Ctx:
+    """arena: a torch uint8 GPU tensor, or (address, bytes) for the host build.
+    stream: a torch.cuda.Stream, a raw hipStream_t int, or None (current stream)."""
+    lib = load_library(kind)
+    if isinstance(arena, tuple):
+        addr, nbytes = arena
+    else:
+        addr, nbytes = arena.data_ptr(), arena.numel() * arena.element_size()
+    if stream is None and kind == "gpu":
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif stream is not None and not isinstance(stream, int):
+        stream = stream.cuda_stream
+    h = _P()
+    rc = lib.skv_create(ctypes.byref(_cfg(cfg)), addr, nbytes, stream, ctypes.byref(h))
+    if rc != 0:
+        raise SkvError(rc, "skv_create")
+    return Ctx(lib, h, cfg, arena, kind)
+
+
+def skv_destroy(ctx: Ctx):
+    if ctx.handle:
+        ctx.lib.skv_destroy(ctx.handle)
+        ctx.handle = None
+
+
+def skv_append_base(ctx: Ctx, layer: int, seq: int, k, v, n: Optional[int] = None):
+    c = ctx.cfg
+    if n is None:
+        n = k.shape[0]
+    shp = (n, c["n_kv_heads"], c["head_dim"])
+    ctx._check(ctx.lib.skv_append_base(ctx.handle, layer, seq, n, _ptr(k, shape=shp, name="k"),
+                                       _ptr(v, shape=shp, name="v")))
+
+
+def skv_append_lowrank(ctx: Ctx, layer: int, seq: int, plane: int, n: int, x=None, A=None):
+    c = ctx.cfg
+    ctx._check(ctx.lib.skv_append_lowrank(
+        ctx.handle, layer, seq, plane, n, _ptr(x, shape=(n, c["hidden"]), name="x"),
+        _ptr(A, shape=(c["hidden"], c["rank"]), name="A")))
+
+
+def skv_append_agents(ctx: Ctx, layer: int, agents: Sequence[int], counts: Sequence[int], k, v,
+                      x=None, A=None):
+    c = ctx.cfg
+    ag, n = _ints(agents)
+    cn, _ = _ints(counts)
+    tot = int(sum(counts))
+    shp = (tot, c["n_kv_heads"], c["head_dim"])
+    a_shape = ((c["n_agents"], c["hidden"], c["rank"]) if c["mode"] == SKV_BASE_SHARED
+               else (c["hidden"], c["rank"]))
+    ctx._check(ctx.lib.skv_append_agents(
+        ctx.handle, layer, n, ag, cn, _ptr(k, shape=shp, name="k"), _ptr(v, shape=shp, name="v"),
+        _ptr(x, shape=(tot, c["hidden"]), name="x"), _ptr(A, shape=a_shape, name="A")))
+
+
+def skv_attn_prefill(ctx: Ctx, layer: int, agents, base_len, suffix_len, n_q, q, B, o):
+    c = ctx.cfg
+    ag, n = _ints(agents)
+    bl, _ = _ints(base_len)
+    sl, _ = _ints(suffix_len)
+    nq, _ = _ints(n_q)
+    rows = int(sum(n_q))
+    qs = (rows, c["n_q_heads"], c["head_dim"])
+    bs = (c["n_agents"], c["rank"], c["n_kv_heads"] * c["head_dim"])
+    ctx._check(ctx.lib.skv_attn_prefill(ctx.handle, layer, n, ag, bl, sl, nq,
+                                        _ptr(q, shape=qs, name="q"), _ptr(B, shape=bs, name="B"),
+                                        _ptr(o, shape=qs, name="o")))
+
+
+def skv_attn_decode(ctx: Ctx, layer: int, agents, base_len, suffix_len, q, B, o):
+    c = ctx.cfg
+    ag, n = _ints(agents)
+    bl, _ = _ints(base_len)
+    sl, _ = _ints(suffix_len)
+    qs = (n, c["n_q_heads"], c["head_dim"])
+    bs = (c["n_agents"], c["rank"], c["n_kv_heads"] * c["head_dim"])
+    ctx._check(ctx.lib.skv_attn_decode(ctx.handle, layer, n, ag, bl, sl,
+                                       _ptr(q, shape=qs, name="q"), _ptr(B, shape=bs, name="B"),
+                                       _ptr(o, shape=qs, name="o")))
+
+
+def skv_crop(ctx: Ctx, seq: int, new_len: int):
+    ctx._check(ctx.lib.skv_crop(ctx.handle, seq, new_len))
+
+
+def skv_get_lens(ctx: Ctx, layer: int) -> dict:
+    N, planes = ctx.cfg["n_agents"], ctx.planes
+    P = ctypes.c_int()
+    b = (ctypes.c_int * N)()
+    S = (ctypes.c_int * N)()
+    ls = (ctypes.c_int * planes)()
+    lo = (ctypes.c_int * N)()
+    ctx._check(ctx.lib.skv_get_lens(ctx.handle, layer, ctypes.byref(P), b, S, ls, lo))
+    return dict(P=P.value, b=list(b), S=list(S), lr_shared=list(ls), lr_own=list(lo))
+
+
+def skv_get_pages(ctx: Ctx, layer: int, seq: int) -> list:
+    n = ctx.lib.skv_get_pages(ctx.handle, layer, seq, None, 0)
+    if n < 0:
+        raise SkvError(n, "skv_get_pages")
+    buf = (ctypes.c_int32 * max(1, n))()
+    ctx.lib.skv_get_pages(ctx.handle, layer, seq, buf, n)
+    return list(buf)[:n]
+
+
+def skv_get_pools(ctx: Ctx) -> dict:
+    p = skv_pools()
+    ctx._check(ctx.lib.skv_get_pools(ctx.handle, ctypes.byref(p)))
+    return {name: getattr(p, name) for name, _ in skv_pools._fields_}
+
+
+def skv_get_counters(ctx: Ctx) -> dict:
+    p = skv_counters()
+    ctx._check(ctx.lib.skv_get_counters(ctx.handle, ctypes.byref(p)))
+    return {name: getattr(p, name) for name, _ in skv_counters._fields_}
+
+
+def skv_set_timing(ctx: Ctx, enable: bool):
+    ctx._check(ctx.lib.skv_set_timing(ctx.handle, 1 if enable else 0))
+
+
+def skv_collect_timing(ctx: Ctx) -> dict:
+    t = skv_kernel_times()
+    ctx._check(ctx.lib.skv_collect_timing(ctx.handle, ctypes.byref(t)))
+    return {k: (t.ms[i], t.launches[i]) for i, k in enumerate(KERNEL_KINDS)}
+
+
+def skv_sync(ctx: Ctx):
+    ctx._check(ctx.lib.skv_sync(ctx.handle))
+
+
+def skv_last_error(ctx: Ctx) -> str:
+    return ctx.lib.skv_last_error(ctx.handle).decode()

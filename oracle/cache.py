@@ -189,17 +189,26 @@ class CacheModel:
         self.lr_cov[layer][seq][plane] = cov + n
 
     def append_agents(self, layer, agents, counts, k, v, x=None, a=None):
-        """Several agents' own rows in one call: same as per-agent appends in order."""
+        """Several agents' own rows in one call: same as per-agent appends in order.
+
+        Checks, in order: arguments; an empty call is a no-op; every agent's own
+        LR rows must be level with its base rows (STATE); pages (OOM).
+        """
         self._check_layer(layer)
-        if len(agents) != len(counts) or len(set(agents)) != len(agents):
+        if len(agents) != len(counts) or len(agents) > self.N:
             raise OracleError("ARG", "agents")
-        for ag, c in zip(agents, counts):
-            self._check_seq(ag)
-            if ag == SHARED or c < 0:
-                raise OracleError("ARG", "agent/count")
+        if len(agents) == 0:
+            return
         if x is not None and a is None:
             raise OracleError("ARG", "A missing")
+        if len(set(agents)) != len(agents):
+            raise OracleError("ARG", "duplicate agent")
+        for ag, c in zip(agents, counts):
+            if not (0 <= ag < self.N) or c < 0:
+                raise OracleError("ARG", "agent/count")
         tot = int(sum(counts))
+        if tot == 0:
+            return
         k = np.asarray(k, dtype=np.float64)
         v = np.asarray(v, dtype=np.float64)
         if k.shape != (tot, self.Hkv, self.d) or v.shape != k.shape:
@@ -210,14 +219,13 @@ class CacheModel:
             ash = (self.N, self.hidden, self.r) if self.mode == BASE_SHARED else (self.hidden, self.r)
             if x.shape != (tot, self.hidden) or a.shape != ash:
                 raise OracleError("ARG", "x/A shape")
+        for ag in agents:
+            if self.lr_cov[layer][ag][self.plane_of(ag)] != self.length[layer][ag]:
+                raise OracleError("STATE", "own low-rank rows lag base rows")
         need = sum(_ceil_div(self.length[layer][ag] + c, self.ps) - len(self.tables[layer][ag])
                    for ag, c in zip(agents, counts))
         if need > len(self.free[layer]):
             raise OracleError("OOM", "page pool exhausted")
-        for ag in agents:
-            p = self.plane_of(ag)
-            if self.lr_cov[layer][ag][p] != self.length[layer][ag]:
-                raise OracleError("STATE", "own low-rank rows lag base rows")
         o = 0
         for ag, c in zip(agents, counts):
             self.append_base(layer, ag, k[o:o + c], v[o:o + c])
@@ -227,7 +235,6 @@ class CacheModel:
                 aa = a[ag] if self.mode == BASE_SHARED else a
                 self.append_lowrank(layer, ag, self.plane_of(ag), c, x[o:o + c], aa)
             o += c
-        assert o == tot
 
     def crop(self, seq, new_len):
         self._check_seq(seq)

@@ -1,0 +1,126 @@
+"""Replays a synthetic schedule through the GPU library (libskv.so) and the oracle.
+
+The GPU side only moves the schedule's bf16 inputs to the device and calls
+the C ABI; the oracle side runs the same events on the CPU in float64. The
+two share nothing but the schedule (synth).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from lora_shared_kv_amd import skv as B
+from synth import (AppendAgents, AppendBase, AppendLowrank, Attend, Crop, Schedule,
+                   bf16_bits_to_f64)
+from oracle.run import apply_event, model_for
+
+MAX_ABS = 2e-2
+MAX_REL_L2 = 1e-2
+
+
+def dev(bits):
+    if bits is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return t.cuda()
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def pages_needed(sc: Schedule, slack=8):
+    """Upper bound of pages per layer over the whole schedule."""
+    s = sc.s
+    rows = {}
+    cur = {}
+    peak = 0
+    for ev in sc.events:
+        if isinstance(ev, AppendBase):
+            key = (ev.layer, ev.seq)
+            cur[key] = cur.get(key, 0) + ev.k.shape[0]
+        elif isinstance(ev, AppendAgents):
+            for a, c in zip(ev.agents, ev.counts):
+                cur[(ev.layer, a)] = cur.get((ev.layer, a), 0) + c
+        elif isinstance(ev, Crop):
+            pass
+        for l in range(sc.L):
+            tot = sum(-(-v // s.page_size) for (ll, _), v in cur.items() if ll == l)
+            peak = max(peak, tot)
+    return peak + slack
+
+
+class GpuRun:
+    def __init__(self, sc: Schedule, max_pages=None):
+        self.sc = sc
+        s = sc.s
+        self.cfg = dict(n_layers=sc.L, n_q_heads=s.n_q_heads, n_kv_heads=s.n_kv_heads,
+                        head_dim=s.head_dim, hidden=s.hidden, rank=s.rank, n_agents=s.n_agents,
+                        mode=s.mode, page_size=s.page_size,
+                        max_pages=max_pages or pages_needed(sc))
+        nbytes = B.skv_arena_bytes(self.cfg)
+        self.arena = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        self.ctx = B.skv_create(self.cfg, self.arena)
+        self._B = {}
+
+    def b_dev(self, ev):
+        key = id(ev.b)
+        if key not in self._B:
+            self._B[key] = dev(ev.b)
+        return self._B[key]
+
+    def apply(self, ev):
+        c = self.ctx
+        if isinstance(ev, AppendBase):
+            B.skv_append_base(c, ev.layer, ev.seq, dev(ev.k), dev(ev.v))
+        elif isinstance(ev, AppendLowrank):
+            B.skv_append_lowrank(c, ev.layer, ev.seq, ev.plane, ev.n, dev(ev.x), dev(ev.a))
+        elif isinstance(ev, AppendAgents):
+            B.skv_append_agents(c, ev.layer, ev.agents, ev.counts, dev(ev.k), dev(ev.v), dev(ev.x),
+                                dev(ev.a))
+        elif isinstance(ev, Crop):
+            B.skv_crop(c, ev.seq, ev.new_len)
+        elif isinstance(ev, Attend):
+            q = dev(ev.q)
+            o = torch.empty_like(q)
+            if ev.kind == "decode":
+                B.skv_attn_decode(c, ev.layer, ev.agents, ev.base_len, ev.suffix_len, q,
+                                  self.b_dev(ev), o)
+            else:
+                B.skv_attn_prefill(c, ev.layer, ev.agents, ev.base_len, ev.suffix_len, ev.n_q, q,
+                                   self.b_dev(ev), o)
+            return o
+        return None
+
+
+def errors(got: np.ndarray, ref: np.ndarray):
+    mask = ~np.isnan(ref[:, 0, 0])
+    g, r = got[mask], ref[mask]
+    assert np.all(np.isfinite(g)), "non-finite GPU output"
+    max_abs = float(np.max(np.abs(g - r))) if g.size else 0.0
+    rel = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)) if g.size else 0.0
+    return max_abs, rel
+
+
+def run_parity(sc: Schedule, sample_rows=None, check=None, max_pages=None, log=None):
+    """Run every event on both sides; compare each attention call. Returns the error list."""
+    gpu = GpuRun(sc, max_pages)
+    orc = model_for(sc.s, sc.L, max_pages=gpu.cfg["max_pages"])
+    results = []
+    for ev in sc.events:
+        o_gpu = gpu.apply(ev)
+        o_ref = apply_event(orc, ev, sample_rows)
+        if o_gpu is not None:
+            got = to_f64(o_gpu)
+            ma, rl = errors(got, o_ref)
+            results.append((ev.tag, ev.kind, ma, rl))
+            if log is not None:
+                log(f"{ev.tag:28s} {ev.kind:8s} max_abs={ma:.3e} rel_l2={rl:.3e}")
+            if check is None:
+                assert ma <= MAX_ABS and rl <= MAX_REL_L2, (ev.tag, ma, rl)
+            else:
+                check(ev, got, o_ref)
+    B.skv_sync(gpu.ctx)
+    return gpu, orc, results
