@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Multi-agent decode throughput of the shared-prefix multi-LoRA attention path.
+
+Workload (default): Llama-3-8B-like attention, 32 layers, 32 query heads,
+8 KV heads, head_dim 128, hidden 4096; 4 agents sharing one down-projection A
+(rank 8, per-agent B_i); a 32,768-token shared prefix. One step is one decode
+token per agent through all 32 layers: for each layer, the four agents' new
+K/V rows and low-rank rows are appended (skv_append_agents) and decode
+attention runs over the shared prefix plus each agent's suffix
+(skv_attn_decode: split pass + merge with B_i). Inputs are synthetic, seeded,
+and already resident in GPU memory when the timed region starts.
+
+Prints one JSON line. `value` = decode tokens/s (agents x steps / wall time).
+`roofline` is for the dominant kernel (the decode split pass): algorithmic
+bytes per launch / its average duration from HIP events recorded around each
+launch on the library's stream during the timed steps, against 8 TB/s.
+`prefill` reports the suffix-prefill kernel (4 agents x 512 tokens at the same
+prefix) against the bf16 MFMA dense peak. `cpu_baseline` times the fp64 CPU
+oracle on a bounded sample of the same decode workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "multi-agent decode tokens/s + % HBM roofline at 32K shared prefix"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+WORKLOADS = {
+    # name: (layers, Hq, Hkv, d, hidden, r, agents, mode, prefix)
+    "llama3-8b-attn-32k": (32, 32, 8, 128, 4096, 8, 4, 1, 32768),
+    "llama3-8b-attn-33k": (32, 32, 8, 128, 4096, 8, 4, 1, 33792),
+    "llama3-8b-attn-66k": (32, 32, 8, 128, 4096, 8, 4, 1, 67584),
+}
+
+
+def decode_split_bytes(Hkv, d, r, prefix, suffixes, n_agents, Hq, bls=True):
+    """Algorithmic bytes one decode split launch must move: the shared K and V
+    rows once per KV head, the low-rank rows (one shared plane, or one per
+    agent), each agent's own K/V/low-rank rows, and the queries."""
+    shared = 4 * Hkv * d * prefix + 2 * r * (prefix if bls else prefix * n_agents)
+    own = sum(s * (4 * Hkv * d + 2 * r) for s in suffixes)
+    return shared + own + 2 * n_agents * Hq * d
+
+
+def prefill_flops(Hq, d, r, views, n_q):
+    """Algorithmic flops of one prefill call: visible causal pairs only."""
+    tot = 0
+    for L, n in zip(views, n_q):
+        pairs = n * (L - n) + n * (n + 1) // 2
+        tot += Hq * ((4 * d + 2 * r) * pairs + 2 * r * d * n)
+    return tot
+
+
+def kernel_hash():
+    p = os.path.join(ROOT, "lora_shared_kv_amd", "csrc", "kernels.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(name):
+    """HBM traffic per launch from committed rocprofv3 counter summaries, if they
+    were taken on the current kernel source; otherwise None."""
+    p = os.path.join(ROOT, "profiles", name)
+    try:
+        rec = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sha") != kernel_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, budget_s=15.0):
+    """The fp64 oracle, as it stands, on one layer of the same decode step."""
+    import numpy as np
+    from oracle.cache import CacheModel
+    from oracle.attention import attention_outputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    L, Hq, Hkv, d, hidden, r, N, mode, prefix = cfg
+    rng = np.random.default_rng(2024)
+    c = CacheModel(1, Hq, Hkv, d, hidden, r, N, mode, 64, prefix // 64 + 64)
+    c.append_base(0, -1, rng.standard_normal((prefix, Hkv, d)), rng.standard_normal((prefix, Hkv, d)))
+    A = rng.standard_normal((hidden, r)) / np.sqrt(hidden)
+    for lo in range(0, prefix, 4096):
+        n = min(4096, prefix - lo)
+        c.append_lowrank(0, -1, 0, n, rng.standard_normal((n, hidden)), A)
+    for a in range(N):
+        c.crop(a, prefix)
+    Bm = rng.standard_normal((N, r, Hkv * d)) * np.sqrt(0.01 / r)
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        k = rng.standard_normal((N, Hkv, d))
+        c.append_agents(0, list(range(N)), [1] * N, k, k, rng.standard_normal((N, hidden)), A)
+        q = rng.standard_normal((N, Hq, d))
+        attention_outputs(c, 0, list(range(N)), [1] * N, q, Bm)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    per_layer = el / steps
+    tok_s = N / (per_layer * L)
+    return {"value": round(tok_s, 4), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{steps} decode steps of 1 layer (4 agents, fp64, prefix {prefix}) timed for "
+                      f"{el:.1f} s; per-layer time x {L} layers"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="llama3-8b-attn-32k", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-events", action="store_true",
+                    help="time the decode steps without per-launch HIP events (no roofline)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from lora_shared_kv_amd import skv as B
+
+    cfg = WORKLOADS[args.workload]
+    L, Hq, Hkv, d, hidden, r, N, mode, prefix = cfg
+    G = Hq // Hkv
+    total_steps = args.warmup + args.steps
+    prefill_n = 512
+    own_max = total_steps + (0 if args.no_prefill else prefill_n)
+    max_pages = prefix // 64 + 1 + N * (own_max // 64 + 2) + 4
+    c = dict(n_layers=L, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, hidden=hidden, rank=r,
+             n_agents=N, mode=mode, page_size=64, max_pages=max_pages)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    arena = torch.empty(B.skv_arena_bytes(c), dtype=torch.uint8, device=dev)
+    ctx = B.skv_create(c, arena, stream)
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1003)
+
+    def randn(*shape, var=1.0):
+        t = torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32)
+        if var != 1.0:
+            t.mul_(var ** 0.5)
+        return t.to(torch.bfloat16)
+
+    # ---- setup: shared prefix (base K/V + low-rank rows with the shared A) ----
+    A = randn(hidden, r, var=1.0 / hidden)
+    Bw = randn(N, r, Hkv * d, var=0.01 / r)
+    chunk = 8192
+    xbuf = randn(chunk, hidden)
+    for l in range(L):
+        for lo in range(0, prefix, chunk):
+            n = min(chunk, prefix - lo)
+            B.skv_append_base(ctx, l, -1, randn(n, Hkv, d), randn(n, Hkv, d))
+            B.skv_append_lowrank(ctx, l, -1, 0, n, xbuf[:n].contiguous(), A)
+    for a in range(N):
+        B.skv_crop(ctx, a, prefix)
+    B.skv_sync(ctx)
+    agents = list(range(N))
+    kin = [randn(N, Hkv, d) for _ in range(L)]
+    vin = [randn(N, Hkv, d) for _ in range(L)]
+    xin = [randn(N, hidden) for _ in range(L)]
+    qin = [randn(N, Hq, d) for _ in range(L)]
+    out = [torch.empty(N, Hq, d, dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    # Device addresses and C int arrays are marshalled once; the step loop only
+    # updates the suffix lengths it passes (and the library checks them).
+    ptr = lambda ts: [t.data_ptr() for t in ts]
+    kp, vp, xp, qp, op = ptr(kin), ptr(vin), ptr(xin), ptr(qin), ptr(out)
+    Ap, Bp = A.data_ptr(), Bw.data_ptr()
+    ag = B.int_array(agents)
+    ones = B.int_array([1] * N)
+    bl = B.int_array([prefix] * N)
+    sl = B.int_array([0] * N)
+    S = [0] * N
+
+    def step():
+        for a in range(N):
+            sl[a] = S[a] + 1
+        for l in range(L):
+            B.skv_append_agents(ctx, l, ag, ones, kp[l], vp[l], xp[l], Ap)
+            B.skv_attn_decode(ctx, l, ag, bl, sl, qp[l], Bp, op[l])
+        for a in range(N):
+            S[a] += 1
+
+    for _ in range(args.warmup):
+        step()
+    B.skv_sync(ctx)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K decode steps, with per-launch HIP events ----
+    suffix_hist = []
+    B.skv_set_timing(ctx, not args.no_events, ["decode_split"])
+    B.skv_collect_timing(ctx)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        suffix_hist.append(S[0] + 1)
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    times = B.skv_collect_timing(ctx)
+    B.skv_set_timing(ctx, False)
+    wall = t1 - t0
+    ms_per_step = 1e3 * wall / args.steps
+    value = N * args.steps / wall
+
+    split_ms, split_n = times["decode_split"]
+    bytes_avg = sum(decode_split_bytes(Hkv, d, r, prefix, [s] * N, N, Hq) for s in suffix_hist) / len(suffix_hist)
+    roofline = None
+    if split_n:
+        avg_split_s = split_ms / 1e3 / split_n
+        achieved = bytes_avg / avg_split_s / 1e9
+        traffic = load_traffic("decode_split_traffic.json")
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "kernel": "decode_split_kernel<128,1,1>",
+                    "algorithmic_bytes_per_launch": int(bytes_avg),
+                    "avg_launch_us": round(avg_split_s * 1e6, 3)}
+    per_kernel = {k: {"ms_total": round(v[0], 3), "launches": v[1],
+                      "avg_us": round(1e3 * v[0] / max(v[1], 1), 3)} for k, v in times.items() if v[1]}
+
+    # ---- suffix prefill: 4 agents x 512 tokens on every layer, same prefix ----
+    prefill = None
+    if not args.no_prefill:
+        kp = randn(N * prefill_n, Hkv, d)
+        xp = randn(N * prefill_n, hidden)
+        qp = randn(N * prefill_n, Hq, d)
+        op = torch.empty_like(qp)
+        for l in range(L):
+            B.skv_append_agents(ctx, l, agents, [prefill_n] * N, kp, kp, xp, A)
+        B.skv_sync(ctx)
+        Ssuf = S[0] + prefill_n
+        B.skv_set_timing(ctx, True)
+        B.skv_collect_timing(ctx)
+        for l in range(L):
+            B.skv_attn_prefill(ctx, l, agents, [prefix] * N, [Ssuf] * N, [prefill_n] * N, qp, Bw, op)
+        pt = B.skv_collect_timing(ctx)
+        B.skv_set_timing(ctx, False)
+        pms, pn = pt["prefill"]
+        fl = prefill_flops(Hq, d, r, [prefix + Ssuf] * N, [prefill_n] * N)
+        tf = fl / (pms / 1e3 / pn) / 1e12
+        prefill = {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                   "frac": round(tf / BF16_PEAK_TFLOPS, 4), "kernel": "prefill_kernel<128,1>",
+                   "flops_per_launch": fl, "avg_launch_ms": round(pms / pn, 4),
+                   "ms_all_layers": round(pms, 3), "n_q_per_agent": prefill_n,
+                   "view": prefix + Ssuf}
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "layers": L, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": d, "hidden": hidden, "rank": r, "agents": N,
+                   "mode": "BaseLRShared" if mode == 1 else "BaseShared", "shared_prefix": prefix,
+                   "decode_tokens_per_step": N, "global_batch": N, "seq_len": prefix,
+                   "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "kernels": per_kernel,
+        "prefill": prefill,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

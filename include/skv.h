@@ -176,10 +176,16 @@ int skv_get_lens(const skv_ctx* ctx, int layer, int* P, int* base_len, int* suff
 int skv_get_pages(const skv_ctx* ctx, int layer, int seq, int32_t* ids, int cap);
 
 /* Device pool layout, for byte-level inspection:
- *   K  [layer][page][Hkv][page_size][d]        bf16
- *   VT [layer][page][Hkv][d][page_size]        bf16 (V stored transposed)
+ *   K  [layer][page][Hkv][64 * d]              bf16 tiles, see below
+ *   V  [layer][page][Hkv][64 * d]              bf16 tiles, see below
  *   LRT[plane][layer][page][r][page_size]      bf16 (low-rank rows transposed)
  *   tables [layer][1 + N][max_pages]           int32 (slot 0 = SHARED)
+ * A (page, head) tile stores its 64 rows in the order the GPU's matrix-core
+ * operand loads read them, so each wave load is 1 KB of contiguous memory.
+ * With key = slot in page (0..63), h = key / 32, kk = key % 32:
+ *   K[key][c] sits at element ((h*2 + t)*(d/32) + c/32)*512 + (n + 16*q)*8 + c%8
+ *     where n = 4*(kk/8) + kk%4, t = (kk%8)/4, q = (c%32)/8;
+ *   V[key][c] sits at element (h*(d/16) + c/16)*512 + (c%16 + 16*(kk/8))*8 + kk%8.
  * Offsets are in bytes from the arena start. */
 typedef struct skv_pools {
   uint64_t k_off, vt_off, lrt_off, tables_off, scratch_off, scratch_bytes, arena_bytes;
@@ -202,6 +208,7 @@ typedef struct skv_kernel_times {
   double ms[SKV_KERNEL_KINDS];
   int64_t launches[SKV_KERNEL_KINDS];
 } skv_kernel_times;
+/* enable: bit mask of kernel kinds to time (bit k = kind k), 0 = off. */
 int skv_set_timing(skv_ctx* ctx, int enable);
 /* Waits for the stream, sums the recorded intervals, and clears them. */
 int skv_collect_timing(skv_ctx* ctx, skv_kernel_times* out);

@@ -78,7 +78,7 @@ int dev_append(const Geometry& g, const AppendJob& job);
 int dev_attn_decode(const Geometry& g, const AttnJob& job);
 int dev_attn_prefill(const Geometry& g, const AttnJob& job);
 int dev_sync(const Geometry& g);
-int dev_set_timing(Geometry& g, bool enable);
+int dev_set_timing(Geometry& g, int mask);
 int dev_collect_timing(Geometry& g, skv_kernel_times* out);
 const char* dev_last_error();
 

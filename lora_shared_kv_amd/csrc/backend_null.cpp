@@ -26,7 +26,7 @@ int dev_attn_prefill(const Geometry& g, const AttnJob&) {
   return SKV_OK;
 }
 int dev_sync(const Geometry&) { return SKV_OK; }
-int dev_set_timing(Geometry&, bool) { return SKV_OK; }
+int dev_set_timing(Geometry&, int) { return SKV_OK; }
 int dev_collect_timing(Geometry&, skv_kernel_times* out) {
   *out = skv_kernel_times{};
   return SKV_OK;

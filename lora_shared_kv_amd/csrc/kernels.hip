@@ -53,7 +53,8 @@ constexpr int kMaxDecodeRows = 64;  // query rows (agents x G) per decode launch
 constexpr int kMaxItems = 2048;     // decode work items per launch (partials capacity)
 constexpr int kMaxMergeSlots = 1024;
 constexpr int kMaxViewPages = 4096;  // prefill view length cap: 262144 tokens
-constexpr int kMaxItemPages = 256;
+constexpr int kMaxItemChunks = 512;  // 32-key chunks per decode item
+constexpr int kCUs = 256;
 
 char g_err[256] = "";
 void set_err(const char* what, hipError_t e) {
@@ -65,6 +66,9 @@ __device__ __forceinline__ u16 f2bf(float f) { return __builtin_bit_cast(u16, (_
 
 __device__ __forceinline__ bf16x8 ld8(const u16* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ bf16x8 ld8_nt(const u16* p) {
+  return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
 }
 __device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0}); }
 
@@ -93,6 +97,30 @@ __device__ __forceinline__ float xsum16_32(float v) {
 // tile entry j of lane group q is key 8q + j (tile 0) or 8q + 4 + j (tile 1).
 __device__ __forceinline__ int perm_key(int m, int t) { return 8 * (m >> 2) + 4 * t + (m & 3); }
 
+// Operand-ordered page tiles. One (page, KV head) tile holds 64 keys x D
+// values of K (or of V) in the order the MFMA operand loads consume them, so
+// every wave-wide 16-byte-per-lane load reads 1 KB of contiguous memory.
+//   K tile: load (half h, score tile t, k-step s) lane (n, q) gets
+//     K[32h + perm_key(n, t)][32s + 8q .. 32s + 8q + 7]
+//     at element ((h * 2 + t) * (D / 32) + s) * 512 + (n + 16q) * 8.
+//   V tile: load (half h, d-block db) lane (n, q) gets
+//     V[32h + 8q .. 32h + 8q + 7][16db + n]  (eight keys of one column)
+//     at element (h * (D / 16) + db) * 512 + (n + 16q) * 8.
+template <int D>
+__device__ __forceinline__ int k_tile_off(int key, int d) {
+  const int h = key >> 5, kk = key & 31;
+  const int n = 4 * (kk >> 3) + (kk & 3), t = (kk & 7) >> 2;
+  const int s = d >> 5, q = (d & 31) >> 3, e = d & 7;
+  return ((h * 2 + t) * (D / 32) + s) * 512 + (n + 16 * q) * 8 + e;
+}
+template <int D>
+__device__ __forceinline__ int v_tile_off(int key, int d) {
+  const int h = key >> 5, kk = key & 31;
+  const int q = kk >> 3, e = kk & 7;
+  const int db = d >> 4, n = d & 15;
+  return (h * (D / 16) + db) * 512 + (n + 16 * q) * 8 + e;
+}
+
 // ---------------------------------------------------------------------------
 // Append: K/V pages + page tables + low-rank rows
 // ---------------------------------------------------------------------------
@@ -120,9 +148,9 @@ struct AppendParams {
 constexpr int kLrTile = 64;   // rows per MFMA low-rank block
 constexpr int kLrChunk = 256; // hidden columns of A staged in LDS per step
 
-__device__ void append_kv_block(const AppendParams& p, int s, int blk, char* smem) {
+template <int D>
+__device__ void append_kv_tile(const AppendParams& p, int s, int blk, char* smem) {
   const skv::Span& sp = p.spans[s];
-  const int D = p.D;
   const int pi = blk / p.Hkv, h = blk % p.Hkv;
   const int page_idx = sp.first_page + pi;
   const int page = p.ids[sp.ids_off + pi];
@@ -131,32 +159,49 @@ __device__ void append_kv_block(const AppendParams& p, int s, int blk, char* sme
   const int hi = (page_idx == (end - 1) / kPage) ? (end - 1) % kPage + 1 : kPage;
   const int rows = hi - lo;
   const int src0 = sp.src_row + (page_idx * kPage + lo - sp.pos0);
-  // K: rows [lo, hi) of the page, 16-byte vectors
+  constexpr int VPR = D / 8;  // 16-byte vectors per row
+  // K: eight consecutive d of one key stay contiguous in the tile
   u16* kdst = p.K + ((uint64_t)page * p.Hkv + h) * kPage * D;
-  const int vec_per_row = D / 8;
-  for (int i = threadIdx.x; i < rows * vec_per_row; i += blockDim.x) {
-    int rr = i / vec_per_row, c = i % vec_per_row;
+  for (int i = threadIdx.x; i < rows * VPR; i += blockDim.x) {
+    const int rr = i / VPR, c = i % VPR;
     const u16* src = p.k + ((uint64_t)(src0 + rr) * p.Hkv + h) * D + c * 8;
-    *reinterpret_cast<u32x4*>(kdst + (uint64_t)(lo + rr) * D + c * 8) =
-        *reinterpret_cast<const u32x4*>(src);
+    *reinterpret_cast<u32x4*>(kdst + k_tile_off<D>(lo + rr, c * 8)) = *reinterpret_cast<const u32x4*>(src);
   }
-  // V: stage the rows in LDS, then write the transposed tile [D][slot]
+  // V: eight consecutive keys of one column are contiguous; stage the rows in
+  // LDS, then write whole 8-key groups as vectors and partial groups by element
   u16* vs = reinterpret_cast<u16*>(smem);  // [64][D + 8]
-  const int ld = D + 8;
-  for (int i = threadIdx.x; i < rows * vec_per_row; i += blockDim.x) {
-    int rr = i / vec_per_row, c = i % vec_per_row;
+  constexpr int ld = D + 8;
+  for (int i = threadIdx.x; i < rows * VPR; i += blockDim.x) {
+    const int rr = i / VPR, c = i % VPR;
     const u16* src = p.v + ((uint64_t)(src0 + rr) * p.Hkv + h) * D + c * 8;
-    u32x4 val = *reinterpret_cast<const u32x4*>(src);
-    u16* dst = vs + rr * ld + c * 8;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(src);
+    u16* dst = vs + (lo + rr) * ld + c * 8;
     *reinterpret_cast<u32x2*>(dst) = u32x2{val[0], val[1]};
     *reinterpret_cast<u32x2*>(dst + 4) = u32x2{val[2], val[3]};
   }
   __syncthreads();
   u16* vdst = p.VT + ((uint64_t)page * p.Hkv + h) * D * kPage;
-  for (int i = threadIdx.x; i < D * rows; i += blockDim.x) {
-    int dd = i / rows, rr = i % rows;
-    vdst[(uint64_t)dd * kPage + lo + rr] = vs[rr * ld + dd];
+  const int g0 = lo >> 3, g1 = (hi + 7) >> 3;  // 8-key groups touched
+  for (int i = threadIdx.x; i < (g1 - g0) * D; i += blockDim.x) {
+    const int grp = g0 + i / D, d = i % D;
+    const int k0 = grp * 8;
+    if (k0 >= lo && k0 + 8 <= hi) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = (uint32_t)vs[(k0 + 2 * e) * ld + d] | ((uint32_t)vs[(k0 + 2 * e + 1) * ld + d] << 16);
+      *reinterpret_cast<u32x4*>(vdst + v_tile_off<D>(k0, d)) = u32x4{w[0], w[1], w[2], w[3]};
+    } else {
+      for (int key = max(k0, lo); key < min(k0 + 8, hi); ++key) vdst[v_tile_off<D>(key, d)] = vs[key * ld + d];
+    }
   }
+}
+
+__device__ void append_kv_block(const AppendParams& p, int s, int blk, char* smem) {
+  if (p.D == 128)
+    append_kv_tile<128>(p, s, blk, smem);
+  else
+    append_kv_tile<64>(p, s, blk, smem);
 }
 
 __device__ void append_lr_zero_block(const AppendParams& p, int s, int pi) {
@@ -174,39 +219,72 @@ __device__ void append_lr_zero_block(const AppendParams& p, int s, int pi) {
   }
 }
 
-// One low-rank row as a block-wide dot product: used when a span has few rows.
-__device__ void append_lr_dot_block(const AppendParams& p, int s, int row, char* smem) {
+// One low-rank row as a block-wide dot product, for spans of a few rows (a
+// decode step appends one row per agent). Each thread takes 8 consecutive
+// hidden columns at a time with 16-byte loads of x and of the matching A rows,
+// so all of a thread's loads are independent and in flight together.
+template <int R>
+__device__ void append_lr_dot_rows(const AppendParams& p, int s, int row, char* smem) {
   const skv::Span& sp = p.spans[s];
-  const int r = p.r, H = p.hidden;
+  const int H = p.hidden;
   const u16* x = p.x + (uint64_t)(sp.src_row + row) * H;
-  float acc[32];
+  constexpr int VR = R >= 8 ? R / 8 : 1;  // 16-byte vectors per A row (r = 4 reads 8 bytes)
+  float acc[R];
 #pragma unroll
-  for (int k = 0; k < 32; ++k) acc[k] = 0.f;
-  for (int u = threadIdx.x; u < H; u += blockDim.x) {
-    float xv = bf2f(x[u]);
-    const u16* arow = sp.a + (uint64_t)u * r;
+  for (int k = 0; k < R; ++k) acc[k] = 0.f;
+#pragma unroll 2
+  for (int u8 = threadIdx.x; u8 < H / 8; u8 += blockDim.x) {
+    const u32x4 xv = *reinterpret_cast<const u32x4*>(x + u8 * 8);
+    const u16* arow = sp.a + (uint64_t)u8 * 8 * R;
+    u32x4 av[8][VR];
 #pragma unroll
-    for (int k = 0; k < 32; ++k)
-      if (k < r) acc[k] += xv * bf2f(arow[k]);
-  }
-  float* red = reinterpret_cast<float*>(smem);  // [4 waves][32]
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    if (k < r) {
-      float v = acc[k];
-      for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-      if (lane == 0) red[w * 32 + k] = v;
+      for (int v = 0; v < VR; ++v) {
+        if (R >= 8) {
+          av[j][v] = *reinterpret_cast<const u32x4*>(arow + j * R + 8 * v);
+        } else {
+          u32x2 t = *reinterpret_cast<const u32x2*>(arow + j * R);
+          av[j][v] = u32x4{t[0], t[1], 0u, 0u};
+        }
+      }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t xw = xv[j / 2];
+      const float xf = __uint_as_float((j & 1) ? (xw & 0xffff0000u) : (xw << 16));
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const uint32_t aw = av[j][k / 8][(k % 8) / 2];
+        acc[k] += xf * __uint_as_float((k & 1) ? (aw & 0xffff0000u) : (aw << 16));
+      }
     }
   }
+  float* red = reinterpret_cast<float*>(smem);  // [waves][R]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    float v = acc[k];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0) red[w * R + k] = v;
+  }
   __syncthreads();
-  if (threadIdx.x < r) {
+  if (threadIdx.x < R) {
     const int k = threadIdx.x;
     float v = 0.f;
-    for (int ww = 0; ww < (int)(blockDim.x >> 6); ++ww) v += red[ww * 32 + k];
+    for (int ww = 0; ww < (int)(blockDim.x >> 6); ++ww) v += red[ww * R + k];
     const int pos = sp.pos0 + row;
     const int page = p.ids[sp.ids_off + pos / kPage - sp.first_page];
-    p.LRT[sp.plane * p.lr_plane + (uint64_t)page * r * kPage + k * kPage + pos % kPage] = f2bf(v);
+    p.LRT[sp.plane * p.lr_plane + (uint64_t)page * R * kPage + k * kPage + pos % kPage] = f2bf(v);
+  }
+}
+
+__device__ void append_lr_dot_block(const AppendParams& p, int s, int row, char* smem) {
+  switch (p.r) {
+    case 4: append_lr_dot_rows<4>(p, s, row, smem); break;
+    case 8: append_lr_dot_rows<8>(p, s, row, smem); break;
+    case 16: append_lr_dot_rows<16>(p, s, row, smem); break;
+    default: append_lr_dot_rows<32>(p, s, row, smem); break;
   }
 }
 
@@ -297,6 +375,12 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 // Decode: split pass
 // ---------------------------------------------------------------------------
 
+// Decode work is cut from one flattened key sequence per KV head: the shared
+// prefix [0, max_b), then each listed agent's own suffix, every segment padded
+// to a multiple of 32 keys. Equal slices of it ("items") go to workgroups, so
+// the grid is balanced whatever the mix of shared and own keys. Each item
+// streams its chunks once for all query rows of the group; a row only takes
+// keys of its own view (shared keys below its b_i, its own suffix keys).
 struct DecodeParams {
   const u16* K;    // layer base [page][Hkv][ps][D]
   const u16* VT;   // layer base [page][Hkv][D][ps]
@@ -314,69 +398,72 @@ struct DecodeParams {
   int ag_pidx[SKV_MAX_AGENTS];    // index of the agent's plane in planes[]
   int n_planes;
   int planes[SKV_MAX_AGENTS];     // stacked low-rank planes of this group
-  int own0[SKV_MAX_AGENTS + 1];   // prefix sums of own items per agent
-  int max_b, split, n_shared, items_per_head;
+  int seg_off[SKV_MAX_AGENTS + 1];  // flattened offset of each own suffix; seg_off[n] = total
+  int shared_len;                 // flattened length of the shared segment (max_b padded)
+  int split, items_per_head;
   float scale_log2;
 };
 
 template <int D, int RB, int MB>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
   constexpr int KS = D / 32, DB = D / 16;
-  __shared__ int32_t s_pages[kMaxItemPages];
-  extern __shared__ __attribute__((aligned(16))) float s_buf[];  // [RB*16][W]
+  __shared__ int32_t s_cpage[kMaxItemChunks];   // page id of each chunk of the item
+  __shared__ int32_t s_ckey[kMaxItemChunks];    // (segment << 24) | first key of the chunk in its segment
+  extern __shared__ __attribute__((aligned(16))) float s_buf[];  // [2][RB*16][W]
 
   const int item = blockIdx.x;
   const int g = item / p.items_per_head;
   const int j = item % p.items_per_head;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = lane & 15, q = lane >> 4;
+  const int total = p.seg_off[p.n];
+  const int f0 = j * p.split;
+  const int n_ck = (min(f0 + p.split, total) - f0) / 32;
 
-  // which key range
-  bool shared = j < p.n_shared;
-  int own_agent = -1, k0, k1;
-  const int32_t* table;
-  if (shared) {
-    k0 = j * p.split;
-    k1 = min(k0 + p.split, p.max_b);
-    table = p.tbl;
-  } else {
-    int jj = j - p.n_shared;
-    int a = 0;
-    while (jj >= p.own0[a + 1]) ++a;
-    own_agent = a;
-    k0 = (jj - p.own0[a]) * p.split;
-    k1 = min(k0 + p.split, p.ag_S[a]);
-    table = p.tbl + (1 + p.ag_id[a]) * p.tbl_seq;
+  // chunk descriptors: segment (0 = shared, 1 + a = agent a's suffix), first key, page
+  for (int c = threadIdx.x; c < n_ck; c += blockDim.x) {
+    const int fc = f0 + 32 * c;
+    int seg = 0, key0 = fc;
+    if (fc >= p.shared_len) {
+      int a = 0;
+      while (fc >= p.seg_off[a + 1]) ++a;
+      seg = 1 + a;
+      key0 = fc - p.seg_off[a];
+    }
+    const int32_t* table = p.tbl + (seg == 0 ? 0 : 1 + p.ag_id[seg - 1]) * p.tbl_seq;
+    s_cpage[c] = table[key0 / kPage];
+    s_ckey[c] = (seg << 24) | key0;
   }
-  const int pg0 = k0 / kPage;
-  const int npg = (k1 - 1) / kPage - pg0 + 1;
-  for (int i = threadIdx.x; i < npg; i += blockDim.x) s_pages[i] = table[pg0 + i];
 
-  // per-lane query rows: Q^T B-operand slices and the row's key limit
+  // per-lane query rows: Q^T B-operand slices, agent and base length of the row
   bf16x8 qf[RB][KS];
-  int lim[RB];
+  int row_agent[RB], row_b[RB], row_S[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int rho = rb * 16 + n;
     const int a = rho / p.G;
-    bool ok = rho < p.R && (shared || a == own_agent);
-    lim[rb] = ok ? min(k1, shared ? p.ag_b[a] : p.ag_S[a]) : 0;
+    const bool ok = rho < p.R;
+    row_agent[rb] = ok ? a : -1;
+    row_b[rb] = ok ? p.ag_b[a] : 0;
+    row_S[rb] = ok ? p.ag_S[a] : 0;
     const u16* qp = p.q + ((uint64_t)a * p.Hq + g * p.G + rho % p.G) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[rb][s] = ok ? ld8(qp + 32 * s + 8 * q) : zero8();
   }
-  // Low-rank A-operand row of this lane in block mb: stacked row sr = 16mb + n.
-  // A shared range stacks every plane of the group (plane sr / r, rank sr % r);
-  // an agent's own range holds only its own plane (rank sr).
-  bool lr_ok[MB];
+  // Low-rank A-operand row of this lane in block mb: stacked row sr = 16mb + n
+  // is rank sr % r of plane sr / r. For an own-suffix chunk the other agents'
+  // planes hold don't-care rows: their products only reach rows that are
+  // masked out for that chunk, or stacked entries a row never keeps. A lane
+  // past the last plane reads a valid row and masks it to zero.
+  uint32_t lr_mask[MB];
   const u16* lr_row[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int sr = mb * 16 + n;
-    const int pi = shared ? sr / p.r : p.ag_pidx[own_agent];
-    const int k = shared ? sr % p.r : sr;
-    lr_ok[mb] = shared ? pi < p.n_planes : sr < p.r;
-    lr_row[mb] = p.LRT + (uint64_t)p.planes[lr_ok[mb] ? pi : 0] * p.lr_plane + k * kPage;
+    const int pi = sr / p.r, k = sr % p.r;
+    const bool ok = pi < p.n_planes;
+    lr_mask[mb] = ok ? 0xffffffffu : 0u;
+    lr_row[mb] = p.LRT + (uint64_t)p.planes[ok ? pi : 0] * p.lr_plane + (ok ? k : 0) * kPage;
   }
 
   float m_run[RB], l_run[RB];
@@ -392,49 +479,54 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
   }
   __syncthreads();
 
-  const int c_begin = k0 / 32 + w, c_end = (k1 + 31) / 32;
   const uint64_t head_off = (uint64_t)g * kPage * D;  // offset of head g inside a page
   const uint64_t page_elems = (uint64_t)p.Hkv * kPage * D;
 
-  bf16x8 kf[2][KS], vf[DB], lf[MB];
-  auto load = [&](int c, bf16x8 (&kk)[2][KS], bf16x8 (&vv)[DB], bf16x8 (&ll)[MB]) {
-    const int key0 = c * 32;
-    const int page = s_pages[key0 / kPage - pg0];
-    const int half = (key0 % kPage) / 32;
-    const u16* kp = p.K + (uint64_t)page * page_elems + head_off + (uint64_t)(half * 32) * D;
+  // Two 32-key chunk buffers per wave: the loop is unrolled by two so the
+  // buffers never need copying, and every prefetch is unconditional (the tail
+  // is peeled), so the compiler keeps the next chunk's loads in flight while
+  // the current chunk is consumed. K and V^T are streamed once, so their
+  // loads are non-temporal.
+  struct Chunk {
+    bf16x8 k[2][KS], v[DB];
+    u32x4 l[MB];  // raw low-rank rows; the lane mask is applied where they are used
+  };
+  auto load = [&](int c, Chunk& ch) {
+    const int page = s_cpage[c];
+    const int half = ((s_ckey[c] & 0xffffff) % kPage) / 32;
+    const u16* kp = p.K + (uint64_t)page * page_elems + head_off + half * (2 * KS * 512) + lane * 8;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int s = 0; s < KS; ++s) kk[t][s] = ld8(kp + perm_key(n, t) * D + 32 * s + 8 * q);
-    const u16* vp = p.VT + (uint64_t)page * page_elems + head_off + half * 32 + 8 * q;
+      for (int s = 0; s < KS; ++s) ch.k[t][s] = ld8_nt(kp + (t * KS + s) * 512);
+    const u16* vp = p.VT + (uint64_t)page * page_elems + head_off + half * (DB * 512) + lane * 8;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) vv[db] = ld8(vp + (db * 16 + n) * kPage);
+    for (int db = 0; db < DB; ++db) ch.v[db] = ld8_nt(vp + db * 512);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
-      ll[mb] = lr_ok[mb] ? ld8(lr_row[mb] + (uint64_t)page * p.r * kPage + half * 32 + 8 * q)
-                         : zero8();
+      ch.l[mb] = *reinterpret_cast<const u32x4*>(lr_row[mb] + (uint64_t)page * p.r * kPage +
+                                                 half * 32 + 8 * q);
   };
-
-  if (c_begin < c_end) load(c_begin, kf, vf, lf);
-  for (int c = c_begin; c < c_end; c += 4) {
-    bf16x8 kn[2][KS], vn[DB], ln[MB];
-    const bool more = c + 4 < c_end;
-    if (more) load(c + 4, kn, vn, ln);
-    const int key0 = c * 32;
+  auto compute = [&](int c, const Chunk& ch) {
+    const int meta = s_ckey[c];
+    const int seg = meta >> 24, key0 = meta & 0xffffff;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
+      // keys of this chunk visible to the lane's row: shared keys below b_i,
+      // or the row's own agent's suffix keys
+      const int lim = seg == 0 ? row_b[rb] : (row_agent[rb] == seg - 1 ? row_S[rb] : 0);
       f32x4 s0 = {0, 0, 0, 0}, s1 = {0, 0, 0, 0};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        s0 = mfma(kf[0][s], qf[rb][s], s0);
-        s1 = mfma(kf[1][s], qf[rb][s], s1);
+        s0 = mfma(ch.k[0][s], qf[rb][s], s0);
+        s1 = mfma(ch.k[1][s], qf[rb][s], s1);
       }
       float sc[8];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int kA = key0 + 8 * q + jj, kB = kA + 4;
-        sc[jj] = kA < lim[rb] ? s0[jj] * p.scale_log2 : -INFINITY;
-        sc[jj + 4] = kB < lim[rb] ? s1[jj] * p.scale_log2 : -INFINITY;
+        sc[jj] = kA < lim ? s0[jj] * p.scale_log2 : -INFINITY;
+        sc[jj + 4] = kB < lim ? s1[jj] * p.scale_log2 : -INFINITY;
       }
       float mx = sc[0];
 #pragma unroll
@@ -452,71 +544,100 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
       m_run[rb] = m_new;
       const bf16x8 pt = pack8(pv);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[rb][db] = mfma(vf[db], pt, oacc[rb][db] * alpha);
+      for (int db = 0; db < DB; ++db) oacc[rb][db] = mfma(ch.v[db], pt, oacc[rb][db] * alpha);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) lacc[rb][mb] = mfma(lf[mb], pt, lacc[rb][mb] * alpha);
+      for (int mb = 0; mb < MB; ++mb)
+        lacc[rb][mb] = mfma(__builtin_bit_cast(bf16x8, ch.l[mb] & lr_mask[mb]), pt, lacc[rb][mb] * alpha);
     }
-    if (more) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int s = 0; s < KS; ++s) kf[t][s] = kn[t][s];
-#pragma unroll
-      for (int db = 0; db < DB; ++db) vf[db] = vn[db];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) lf[mb] = ln[mb];
+  };
+  const int n_chunks = w < n_ck ? (n_ck - w + 3) / 4 : 0;  // this wave's chunks: w, w + 4, ...
+  if (n_chunks > 0) {
+    Chunk A, Bf;
+    load(w, A);
+    int i = 0;
+    // sched_barrier keeps each prefetch ahead of the wait for the buffer in use
+    for (; i + 2 < n_chunks; i += 2) {
+      load(w + 4 * (i + 1), Bf);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(w + 4 * i, A);
+      load(w + 4 * (i + 2), A);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(w + 4 * (i + 1), Bf);
+    }
+    if (n_chunks - i == 2) {
+      load(w + 4 * (i + 1), Bf);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(w + 4 * i, A);
+      compute(w + 4 * (i + 1), Bf);
+    } else {
+      compute(w + 4 * i, A);
     }
   }
 
-  // Combine the four waves' states in LDS, one wave at a time (deterministic).
+  // Combine the four waves: waves 2 and 3 park their states in LDS, waves 0
+  // and 1 fold them in, then every thread merges the two remaining states
+  // and writes the item's partial rows (o, o_lr, m, l) for the merge pass.
   const int W = p.W;
+  const int RP = RB * 16;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) l_run[rb] = xsum16_32(l_run[rb]);
-  for (int ww = 0; ww < 4; ++ww) {
-    if (w == ww) {
+  auto park = [&](float* buf, bool fold) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int rho = rb * 16 + n;
-        float* row = s_buf + rho * W;
-        const int a = min(rho / p.G, p.n - 1);
-        const int pidx = p.ag_pidx[a];
-        float a_old = 0.f, a_new = 1.f, m_c = m_run[rb];
-        if (ww > 0) {
-          const float m_old = row[D + p.r];
-          m_c = fmaxf(m_old, m_run[rb]);
-          a_old = __builtin_amdgcn_exp2f(m_old - m_c);
-          a_new = __builtin_amdgcn_exp2f(m_run[rb] - m_c);
+    for (int rb = 0; rb < RB; ++rb) {
+      const int rho = rb * 16 + n;
+      float* row = buf + rho * W;
+      const int a = min(rho / p.G, p.n - 1);
+      const int pidx = p.ag_pidx[a];
+      float a_old = 0.f, a_new = 1.f, m_c = m_run[rb];
+      if (fold) {
+        const float m_old = row[D + p.r];
+        m_c = fmaxf(m_old, m_run[rb]);
+        a_old = __builtin_amdgcn_exp2f(m_old - m_c);
+        a_new = __builtin_amdgcn_exp2f(m_run[rb] - m_c);
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          float* dst = row + db * 16 + 4 * q + jj;
+          *dst = (fold ? a_old * *dst : 0.f) + a_new * oacc[rb][db][jj];
         }
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            float* dst = row + db * 16 + 4 * q + jj;
-            *dst = (ww > 0 ? a_old * *dst : 0.f) + a_new * oacc[rb][db][jj];
+        for (int jj = 0; jj < 4; ++jj) {
+          const int sr = mb * 16 + 4 * q + jj;
+          if (sr / p.r == pidx) {
+            float* dst = row + D + sr % p.r;
+            *dst = (fold ? a_old * *dst : 0.f) + a_new * lacc[rb][mb][jj];
           }
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int sr = mb * 16 + 4 * q + jj;
-            const int want = shared ? pidx : 0;
-            if (sr / p.r == want && sr < p.n_planes * p.r) {
-              float* dst = row + D + sr % p.r;
-              *dst = (ww > 0 ? a_old * *dst : 0.f) + a_new * lacc[rb][mb][jj];
-            }
-          }
-        if (q == 0) {
-          const float l_old = ww > 0 ? row[D + p.r + 1] : 0.f;
-          row[D + p.r + 1] = a_old * l_old + a_new * l_run[rb];
-          row[D + p.r] = m_c;
         }
+      if (q == 0) {
+        const float l_old = fold ? row[D + p.r + 1] : 0.f;
+        row[D + p.r + 1] = a_old * l_old + a_new * l_run[rb];
+        row[D + p.r] = m_c;
       }
     }
-    __syncthreads();
-  }
-  // write the partial rows
+  };
+  if (w >= 2) park(s_buf + (w - 2) * RP * W, false);
+  __syncthreads();
+  if (w < 2) park(s_buf + w * RP * W, true);
+  __syncthreads();
   float* dst = p.part + (uint64_t)item * p.R * W;
-  for (int i = threadIdx.x; i < p.R * W; i += blockDim.x) dst[i] = s_buf[i];
+  const float* b0 = s_buf;
+  const float* b1 = s_buf + RP * W;
+  const int E = D + p.r;
+  for (int i = threadIdx.x; i < p.R * E; i += blockDim.x) {
+    const int rho = i / E, e = i % E;
+    const float m0 = b0[rho * W + E], m1 = b1[rho * W + E];
+    const float mc = fmaxf(m0, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m0 - mc), a1 = __builtin_amdgcn_exp2f(m1 - mc);
+    dst[rho * W + e] = a0 * b0[rho * W + e] + a1 * b1[rho * W + e];
+    if (e == 0) {
+      dst[rho * W + E] = mc;
+      dst[rho * W + E + 1] = a0 * b0[rho * W + E + 1] + a1 * b1[rho * W + E + 1];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -530,64 +651,79 @@ struct MergeParams {
   int Hkv, Hq, G, D, r, R, W;
   int n;
   int ag_id[SKV_MAX_AGENTS];
-  int own0[SKV_MAX_AGENTS + 1];
-  int n_shared, items_per_head;
+  int items_per_head;
 };
 
+// One workgroup per query row (agent, query head). Merges the row's partial
+// softmax states from every item of its KV head: M = max m_s, weights w_s = 2^(m_s - M)
+// / sum_s 2^(m_s - M) l_s, o = sum_s w_s o_s and o_lr = sum_s w_s o_lr,s; then
+// applies B_i once: o[d] += sum_k o_lr[k] B_i[k][g*D + d], rounded to bf16.
 __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
-  __shared__ float s_w[8][kMaxMergeSlots];
-  __shared__ float s_lr[8][32];
-  __shared__ float s_o[8][128];
-  const int a = blockIdx.x / p.Hkv, g = blockIdx.x % p.Hkv;
+  __shared__ float s_w[kMaxMergeSlots];
+  __shared__ f32x4 s_red[8][40];
+  __shared__ float s_v[128 + 32];
+  __shared__ float s_m[4];
+  const int row_id = blockIdx.x;
+  const int hh = row_id % p.G;
+  const int g = (row_id / p.G) % p.Hkv;
+  const int a = row_id / (p.G * p.Hkv);
+  const int rho = a * p.G + hh;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int n_own = p.own0[a + 1] - p.own0[a];
-  const int n_slots = p.n_shared + n_own;
-  auto slot_item = [&](int s) {
-    return g * p.items_per_head + (s < p.n_shared ? s : p.n_shared + p.own0[a] + (s - p.n_shared));
+  const int n_slots = p.items_per_head;
+  auto slot_row = [&](int s) {
+    return p.part + ((uint64_t)(g * p.items_per_head + s) * p.R + rho) * p.W;
   };
+  // weights
+  float M = -1e30f;
+  for (int s = threadIdx.x; s < n_slots; s += blockDim.x) {
+    const float m = slot_row(s)[p.D + p.r];
+    s_w[s] = m;
+    M = fmaxf(M, m);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if (lane == 0) s_m[w] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  float L = 0.f;
+  for (int s = threadIdx.x; s < n_slots; s += blockDim.x) {
+    const float e = __builtin_amdgcn_exp2f(s_w[s] - M);
+    s_w[s] = e;
+    L += e * slot_row(s)[p.D + p.r + 1];
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+  __syncthreads();
+  if (lane == 0) s_m[w] = L;
+  __syncthreads();
+  const float inv = 1.f / (s_m[0] + s_m[1] + s_m[2] + s_m[3]);
+  // weighted sums: element quads x slot groups
+  const int NQ = (p.D + p.r) / 4;
+  const int NG = min(8, (int)blockDim.x / NQ);
+  const int qd = threadIdx.x % NQ, sg = threadIdx.x / NQ;
+  if (sg < NG) {
+    f32x4 acc = {0, 0, 0, 0};
+#pragma unroll 4
+    for (int s = sg; s < n_slots; s += NG) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(slot_row(s) + 4 * qd);
+      acc += s_w[s] * v;
+    }
+    s_red[sg][qd] = acc;
+  }
+  __syncthreads();
+  if (threadIdx.x < NQ) {
+    f32x4 acc = s_red[0][threadIdx.x];
+    for (int gg = 1; gg < NG; ++gg) acc += s_red[gg][threadIdx.x];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s_v[4 * threadIdx.x + j] = acc[j] * inv;
+  }
+  __syncthreads();
   const int HD = p.Hkv * p.D;
-  for (int h0 = 0; h0 < p.G; h0 += 8) {
-    const int nr = min(8, p.G - h0);
-    // weights per (row, slot): exp2(m_s - M) / L
-    for (int rr = w; rr < nr; rr += 4) {
-      const int rho = a * p.G + h0 + rr;
-      float M = -1e30f;
-      for (int s = lane; s < n_slots; s += 64)
-        M = fmaxf(M, p.part[((uint64_t)slot_item(s) * p.R + rho) * p.W + p.D + p.r]);
-      for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-      float L = 0.f;
-      for (int s = lane; s < n_slots; s += 64) {
-        const float* row = p.part + ((uint64_t)slot_item(s) * p.R + rho) * p.W;
-        float e = __builtin_amdgcn_exp2f(row[p.D + p.r] - M);
-        s_w[rr][s] = e;
-        L += e * row[p.D + p.r + 1];
-      }
-      for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
-      const float inv = 1.f / L;
-      for (int s = lane; s < n_slots; s += 64) s_w[rr][s] *= inv;
-    }
-    __syncthreads();
-    const int E = p.D + p.r;
-    for (int i = threadIdx.x; i < nr * E; i += blockDim.x) {
-      const int rr = i / E, e = i % E;
-      const int rho = a * p.G + h0 + rr;
-      float acc = 0.f;
-      for (int s = 0; s < n_slots; ++s)
-        acc += s_w[rr][s] * p.part[((uint64_t)slot_item(s) * p.R + rho) * p.W + e];
-      if (e < p.D)
-        s_o[rr][e] = acc;
-      else
-        s_lr[rr][e - p.D] = acc;
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < nr * p.D; i += blockDim.x) {
-      const int rr = i / p.D, d = i % p.D;
-      float acc = s_o[rr][d];
-      const u16* bcol = p.B + (uint64_t)p.ag_id[a] * p.r * HD + g * p.D + d;
-      for (int k = 0; k < p.r; ++k) acc += s_lr[rr][k] * bf2f(bcol[(uint64_t)k * HD]);
-      p.o[((uint64_t)a * p.Hq + g * p.G + h0 + rr) * p.D + d] = f2bf(acc);
-    }
-    __syncthreads();
+  for (int d = threadIdx.x; d < p.D; d += blockDim.x) {
+    float out = s_v[d];
+    const u16* bcol = p.B + (uint64_t)p.ag_id[a] * p.r * HD + g * p.D + d;
+    for (int k = 0; k < p.r; ++k) out += s_v[p.D + k] * bf2f(bcol[(uint64_t)k * HD]);
+    p.o[((uint64_t)a * p.Hq + g * p.G + hh) * p.D + d] = f2bf(out);
   }
 }
 
@@ -687,15 +823,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
       const int key0 = c * 32;
       const int page = s_pages[pg_off + key0 / kPage];
       const int half = (key0 % kPage) / 32;
-      const u16* kp = p.K + (uint64_t)page * page_elems + head_off + (uint64_t)(half * 32) * D;
+      const u16* kp = p.K + (uint64_t)page * page_elems + head_off + half * (2 * KS * 512) + lane * 8;
       bf16x8 kf[2][KS], vf[DB], lf[MB];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int s = 0; s < KS; ++s) kf[t][s] = ld8(kp + perm_key(n, t) * D + 32 * s + 8 * q);
-      const u16* vp = p.VT + (uint64_t)page * page_elems + head_off + half * 32 + 8 * q;
+        for (int s = 0; s < KS; ++s) kf[t][s] = ld8(kp + (t * KS + s) * 512);
+      const u16* vp = p.VT + (uint64_t)page * page_elems + head_off + half * (DB * 512) + lane * 8;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) vf[db] = ld8(vp + (db * 16 + n) * kPage);
+      for (int db = 0; db < DB; ++db) vf[db] = ld8(vp + db * 512);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
         lf[mb] = lr_ok[mb] ? ld8(lrb + (uint64_t)page * p.r * kPage + (mb * 16 + n) * kPage +
@@ -790,7 +926,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
 // ---------------------------------------------------------------------------
 
 struct DevState {
-  bool timing = false;
+  int timing = 0;  // bit mask of kernel kinds to time
   std::vector<hipEvent_t> pool;
   struct Rec {
     int kind;
@@ -816,7 +952,7 @@ struct TimedLaunch {
   hipEvent_t a = nullptr, b = nullptr;
   TimedLaunch(const skv::Geometry& g, int k)
       : st((DevState*)g.dev), stream((hipStream_t)g.stream), kind(k) {
-    if (st && st->timing) {
+    if (st && (st->timing >> k & 1)) {
       a = st->get();
       b = st->get();
       if (a && b) (void)hipEventRecord(a, stream);
@@ -854,7 +990,7 @@ int w_of(const skv::Geometry& g) { return g.D + g.r + 4; }
 
 template <int D, int RB, int MB>
 void launch_split_t(const DecodeParams& p, int items, hipStream_t st) {
-  size_t lds = (size_t)RB * 16 * p.W * sizeof(float);
+  size_t lds = (size_t)2 * RB * 16 * p.W * sizeof(float);
   hipLaunchKernelGGL((decode_split_kernel<D, RB, MB>), dim3(items), dim3(256), lds, st, p);
 }
 
@@ -990,7 +1126,7 @@ int dev_attn_decode(const Geometry& g, const AttnJob& job) {
     p.W = W;
     p.n = n;
     p.n_planes = 0;
-    int max_b = 0, own_keys = 0;
+    int max_b = 0;
     for (int i = 0; i < n; ++i) {
       const AttnAgent& a = job.ag[a0 + i];
       p.ag_id[i] = a.agent;
@@ -1005,33 +1141,24 @@ int dev_attn_decode(const Geometry& g, const AttnJob& job) {
       }
       p.ag_pidx[i] = pidx;
       max_b = std::max(max_b, a.b);
-      own_keys += a.S;
     }
-    p.max_b = max_b;
-    // split plan: about 2 workgroups per CU over all KV heads, 256-key granularity
-    const int target_per_head = std::max(1, 512 / g.Hkv);
-    const int keys = max_b + own_keys;
-    int split = ((keys + target_per_head - 1) / target_per_head + 255) / 256 * 256;
-    split = std::max(split, 256);
-    int items_per_head = 0;
-    for (;;) {
-      int ns = (max_b + split - 1) / split;
-      int no = 0;
-      for (int i = 0; i < n; ++i) no += (p.ag_S[i] + split - 1) / split;
-      items_per_head = ns + no;
-      if ((uint64_t)items_per_head * g.Hkv <= (uint64_t)kMaxItems &&
-          items_per_head <= kMaxMergeSlots)
-        break;
-      split *= 2;
-    }
-    if (split / kPage > kMaxItemPages) {
-      snprintf(g_err, sizeof g_err, "decode view too long for the split plan (%d keys)", keys);
+    // flattened key sequence per KV head: shared prefix, then each own suffix,
+    // each padded to whole 32-key chunks
+    p.shared_len = (max_b + 31) / 32 * 32;
+    p.seg_off[0] = p.shared_len;
+    for (int i = 0; i < n; ++i) p.seg_off[i + 1] = p.seg_off[i] + (p.ag_S[i] + 31) / 32 * 32;
+    const int total = p.seg_off[n];
+    // items: about one per CU over all KV heads, in whole 32-key chunks
+    const int chunks = total / 32;
+    int per_head = std::max(1, std::min(chunks, kCUs / g.Hkv));
+    int split = (chunks + per_head - 1) / per_head * 32;
+    if (split > kMaxItemChunks * 32) split = kMaxItemChunks * 32;
+    const int items_per_head = (total + split - 1) / split;
+    if ((uint64_t)items_per_head * g.Hkv > (uint64_t)kMaxItems || items_per_head > kMaxMergeSlots) {
+      snprintf(g_err, sizeof g_err, "decode view too long for the split plan (%d keys)", total);
       return SKV_ERR_UNSUPPORTED;
     }
     p.split = split;
-    p.n_shared = (max_b + split - 1) / split;
-    p.own0[0] = 0;
-    for (int i = 0; i < n; ++i) p.own0[i + 1] = p.own0[i] + (p.ag_S[i] + split - 1) / split;
     p.items_per_head = items_per_head;
     p.scale_log2 = 1.4426950408889634f / sqrtf((float)g.D);
     int rb = (p.R + 15) / 16;
@@ -1064,12 +1191,10 @@ int dev_attn_decode(const Geometry& g, const AttnJob& job) {
     mp.W = W;
     mp.n = n;
     for (int i = 0; i < n; ++i) mp.ag_id[i] = p.ag_id[i];
-    for (int i = 0; i <= n; ++i) mp.own0[i] = p.own0[i];
-    mp.n_shared = p.n_shared;
     mp.items_per_head = items_per_head;
     {
       TimedLaunch t(g, 3);
-      hipLaunchKernelGGL(decode_merge_kernel, dim3(n * g.Hkv), dim3(256), 0, st, mp);
+      hipLaunchKernelGGL(decode_merge_kernel, dim3(n * g.Hkv * g.G), dim3(256), 0, st, mp);
       ++*g.launches;
       int rc = t.done("decode_merge_kernel");
       if (rc != SKV_OK) return rc;
@@ -1135,9 +1260,9 @@ int dev_sync(const Geometry& g) {
   return SKV_OK;
 }
 
-int dev_set_timing(Geometry& g, bool enable) {
+int dev_set_timing(Geometry& g, int mask) {
   auto* st = (DevState*)g.dev;
-  st->timing = enable;
+  st->timing = mask;
   return SKV_OK;
 }
 

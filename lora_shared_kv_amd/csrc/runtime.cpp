@@ -302,12 +302,12 @@ int skv_append_agents(skv_ctx* c, int layer, int n, const int* agents, const int
   if (n == 0) return SKV_OK;
   if (!agents || !counts) return c->fail(SKV_ERR_ARG, "null agents or counts");
   if (x && !A) return c->fail(SKV_ERR_ARG, "x given without A");
-  std::vector<bool> seen(g.N, false);
+  uint32_t seen = 0;
   long total = 0;
   for (int i = 0; i < n; ++i) {
     int a = agents[i];
-    if (a >= 0 && a < g.N && seen[a]) return c->fail(SKV_ERR_ARG, "duplicate agent %d", a);
-    if (a >= 0 && a < g.N) seen[a] = true;
+    if (a >= 0 && a < g.N && (seen >> a & 1u)) return c->fail(SKV_ERR_ARG, "duplicate agent %d", a);
+    if (a >= 0 && a < g.N) seen |= 1u << a;
   }
   for (int i = 0; i < n; ++i) {
     int a = agents[i];
@@ -389,13 +389,12 @@ static int validate_attend(skv_ctx* c, int layer, int n, const int* agents, cons
   if (!agents || !base_len || !suffix_len || !q || !B || !o)
     return c->fail(SKV_ERR_ARG, "null argument");
   const Layer& l = c->layers[layer];
-  std::vector<bool> seen(g.N, false);
+  uint32_t seen = 0;
   for (int i = 0; i < n; ++i) {
     int a = agents[i];
-    if (a >= 0 && a < g.N && seen[a]) return c->fail(SKV_ERR_ARG, "duplicate agent %d", a);
-    if (a >= 0 && a < g.N) seen[a] = true;
+    if (a >= 0 && a < g.N && (seen >> a & 1u)) return c->fail(SKV_ERR_ARG, "duplicate agent %d", a);
+    if (a >= 0 && a < g.N) seen |= 1u << a;
   }
-  job = AttnJob{};
   job.layer = layer;
   job.n = n;
   int row = 0;
@@ -535,7 +534,7 @@ int skv_get_counters(const skv_ctx* c, skv_counters* out) {
 
 int skv_set_timing(skv_ctx* c, int enable) {
   if (!c) return SKV_ERR_ARG;
-  return skv::dev_set_timing(c->g, enable != 0);
+  return skv::dev_set_timing(c->g, enable);
 }
 
 int skv_collect_timing(skv_ctx* c, skv_kernel_times* out) {

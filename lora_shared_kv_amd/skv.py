@@ -99,25 +99,40 @@ class SkvError(RuntimeError):
         super().__init__(f"skv error {self.code}: {msg}")
 
 
+_torch = None
+_bf16 = None
+
+
 def _ints(xs):
+    """A C int array for a host int list; a ctypes array passes through unchanged."""
+    if isinstance(xs, ctypes.Array):
+        return xs, len(xs)
     xs = [int(x) for x in xs]
     return (ctypes.c_int * max(1, len(xs)))(*xs), len(xs)
 
 
-def _ptr(t, kind=None, shape=None, name="tensor"):
+def int_array(xs):
+    """Build a reusable C int array (for calls repeated in a loop)."""
+    return (ctypes.c_int * max(1, len(xs)))(*[int(x) for x in xs])
+
+
+def _ptr(t, shape=None, name="tensor"):
     """Device pointer of a tensor (checked) or an int address; None -> NULL."""
+    global _torch, _bf16
     if t is None:
         return None
     if isinstance(t, int):
         return t
-    import torch
-    if t.dtype != torch.bfloat16:
+    if _torch is None:
+        import torch
+        _torch, _bf16 = torch, torch.bfloat16
+    if t.dtype is not _bf16:
         raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
     if not t.is_cuda:
         raise TypeError(f"{name} must be a GPU tensor")
     if not t.is_contiguous():
         raise TypeError(f"{name} must be contiguous")
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != shape:
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     return t.data_ptr()
 
@@ -130,6 +145,11 @@ class Ctx:
         c = self.cfg
         self.G = c["n_q_heads"] // c["n_kv_heads"]
         self.planes = c["n_agents"] if c["mode"] == SKV_BASE_SHARED else 1
+        self.Hq, self.Hkv, self.d = c["n_q_heads"], c["n_kv_heads"], c["head_dim"]
+        self.hidden, self.r, self.N = c["hidden"], c["rank"], c["n_agents"]
+        self.b_shape = (self.N, self.r, self.Hkv * self.d)
+        self.a_shape = ((self.N, self.hidden, self.r) if c["mode"] == SKV_BASE_SHARED
+                        else (self.hidden, self.r))
 
     def _check(self, rc):
         if rc != 0:
@@ -196,44 +216,33 @@ def skv_append_lowrank(ctx: Ctx, layer: int, seq: int, plane: int, n: int, x=Non
         _ptr(A, shape=(c["hidden"], c["rank"]), name="A")))
 
 
-def skv_append_agents(ctx: Ctx, layer: int, agents: Sequence[int], counts: Sequence[int], k, v,
-                      x=None, A=None):
-    c = ctx.cfg
+def skv_append_agents(ctx: Ctx, layer: int, agents, counts, k, v, x=None, A=None):
     ag, n = _ints(agents)
     cn, _ = _ints(counts)
-    tot = int(sum(counts))
-    shp = (tot, c["n_kv_heads"], c["head_dim"])
-    a_shape = ((c["n_agents"], c["hidden"], c["rank"]) if c["mode"] == SKV_BASE_SHARED
-               else (c["hidden"], c["rank"]))
+    tot = sum(cn[:n])
+    shp = (tot, ctx.Hkv, ctx.d)
     ctx._check(ctx.lib.skv_append_agents(
-        ctx.handle, layer, n, ag, cn, _ptr(k, shape=shp, name="k"), _ptr(v, shape=shp, name="v"),
-        _ptr(x, shape=(tot, c["hidden"]), name="x"), _ptr(A, shape=a_shape, name="A")))
+        ctx.handle, layer, n, ag, cn, _ptr(k, shp, "k"), _ptr(v, shp, "v"),
+        _ptr(x, (tot, ctx.hidden), "x"), _ptr(A, ctx.a_shape, "A")))
 
 
 def skv_attn_prefill(ctx: Ctx, layer: int, agents, base_len, suffix_len, n_q, q, B, o):
-    c = ctx.cfg
     ag, n = _ints(agents)
     bl, _ = _ints(base_len)
     sl, _ = _ints(suffix_len)
     nq, _ = _ints(n_q)
-    rows = int(sum(n_q))
-    qs = (rows, c["n_q_heads"], c["head_dim"])
-    bs = (c["n_agents"], c["rank"], c["n_kv_heads"] * c["head_dim"])
-    ctx._check(ctx.lib.skv_attn_prefill(ctx.handle, layer, n, ag, bl, sl, nq,
-                                        _ptr(q, shape=qs, name="q"), _ptr(B, shape=bs, name="B"),
-                                        _ptr(o, shape=qs, name="o")))
+    qs = (sum(nq[:n]), ctx.Hq, ctx.d)
+    ctx._check(ctx.lib.skv_attn_prefill(ctx.handle, layer, n, ag, bl, sl, nq, _ptr(q, qs, "q"),
+                                        _ptr(B, ctx.b_shape, "B"), _ptr(o, qs, "o")))
 
 
 def skv_attn_decode(ctx: Ctx, layer: int, agents, base_len, suffix_len, q, B, o):
-    c = ctx.cfg
     ag, n = _ints(agents)
     bl, _ = _ints(base_len)
     sl, _ = _ints(suffix_len)
-    qs = (n, c["n_q_heads"], c["head_dim"])
-    bs = (c["n_agents"], c["rank"], c["n_kv_heads"] * c["head_dim"])
-    ctx._check(ctx.lib.skv_attn_decode(ctx.handle, layer, n, ag, bl, sl,
-                                       _ptr(q, shape=qs, name="q"), _ptr(B, shape=bs, name="B"),
-                                       _ptr(o, shape=qs, name="o")))
+    qs = (n, ctx.Hq, ctx.d)
+    ctx._check(ctx.lib.skv_attn_decode(ctx.handle, layer, n, ag, bl, sl, _ptr(q, qs, "q"),
+                                       _ptr(B, ctx.b_shape, "B"), _ptr(o, qs, "o")))
 
 
 def skv_crop(ctx: Ctx, seq: int, new_len: int):
@@ -272,8 +281,15 @@ def skv_get_counters(ctx: Ctx) -> dict:
     return {name: getattr(p, name) for name, _ in skv_counters._fields_}
 
 
-def skv_set_timing(ctx: Ctx, enable: bool):
-    ctx._check(ctx.lib.skv_set_timing(ctx.handle, 1 if enable else 0))
+def skv_set_timing(ctx: Ctx, enable, kinds=None):
+    """Record HIP events around launches of the given kernel kinds (names from
+    KERNEL_KINDS; default all) while enabled."""
+    mask = 0
+    if enable:
+        kinds = KERNEL_KINDS if kinds is None else kinds
+        for k in kinds:
+            mask |= 1 << KERNEL_KINDS.index(k)
+    ctx._check(ctx.lib.skv_set_timing(ctx.handle, mask))
 
 
 def skv_collect_timing(ctx: Ctx) -> dict:

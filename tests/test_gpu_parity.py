@@ -179,7 +179,25 @@ def test_lr_contribution_difference():
 # layout, low-rank rows, determinism, sharing
 # --------------------------------------------------------------------------
 
+def k_tile_index(D):
+    """Element offset of K[key][c] inside a (page, head) tile (layout in include/skv.h)."""
+    key = np.arange(64)[:, None]
+    c = np.arange(D)[None, :]
+    h, kk = key >> 5, key & 31
+    n, t = 4 * (kk >> 3) + (kk & 3), (kk & 7) >> 2
+    return ((h * 2 + t) * (D // 32) + (c >> 5)) * 512 + (n + 16 * ((c & 31) >> 3)) * 8 + (c & 7)
+
+
+def v_tile_index(D):
+    """Element offset of V[key][c] inside a (page, head) tile (layout in include/skv.h)."""
+    key = np.arange(64)[:, None]
+    c = np.arange(D)[None, :]
+    h, kk = key >> 5, key & 31
+    return (h * (D // 16) + (c >> 4)) * 512 + ((c & 15) + 16 * (kk >> 3)) * 8 + (kk & 7)
+
+
 def _pool_views(gpu):
+    """Raw pools: K and V as [layer][page][head][64 * d] tiles, LRT as [plane][layer][page][r][64]."""
     import torch
     from lora_shared_kv_amd import skv as B
     c = gpu.cfg
@@ -187,8 +205,8 @@ def _pool_views(gpu):
     L, mp, Hkv, d, r = c["n_layers"], c["max_pages"], c["n_kv_heads"], c["head_dim"], c["rank"]
     a16 = gpu.arena.view(torch.int16)
     kn = L * mp * Hkv * 64 * d
-    K = a16[p["k_off"] // 2: p["k_off"] // 2 + kn].view(L, mp, Hkv, 64, d)
-    VT = a16[p["vt_off"] // 2: p["vt_off"] // 2 + kn].view(L, mp, Hkv, d, 64)
+    K = a16[p["k_off"] // 2: p["k_off"] // 2 + kn].view(L, mp, Hkv, 64 * d)
+    VT = a16[p["vt_off"] // 2: p["vt_off"] // 2 + kn].view(L, mp, Hkv, 64 * d)
     ln = p["planes"] * L * mp * r * 64
     LRT = a16[p["lrt_off"] // 2: p["lrt_off"] // 2 + ln].view(p["planes"], L, mp, r, 64)
     return K, VT, LRT
@@ -201,12 +219,14 @@ def test_cache_layout_bytes_and_lowrank_rows():
     sc = mini(shape, 333, [70, 5], decode_steps=2)
     gpu, orc, _ = R.run_parity(sc)
     K, VT, LRT = (t.cpu().numpy().view(np.uint16) for t in _pool_views(gpu))
+    d = shape.head_dim
+    ki, vi = k_tile_index(d), v_tile_index(d)
     for seq in [-1, 0, 1]:
         pages = B.skv_get_pages(gpu.ctx, 0, seq)
         assert pages == orc.pages(0, seq)
         n = orc.length[0][seq]
-        kk = np.stack([K[0, pages[j // 64], :, j % 64, :] for j in range(n)])
-        vv = np.stack([VT[0, pages[j // 64], :, :, j % 64] for j in range(n)])
+        kk = np.stack([K[0, pages[j // 64]][:, ki[j % 64]] for j in range(n)])
+        vv = np.stack([VT[0, pages[j // 64]][:, vi[j % 64]] for j in range(n)])
         assert np.array_equal(bf16_bits_to_f64(kk), orc.k[0][seq].get(n)), seq
         assert np.array_equal(bf16_bits_to_f64(vv), orc.v[0][seq].get(n)), seq
         for p in orc._planes_of(seq):
