@@ -43,13 +43,16 @@ WORKLOADS = {
 }
 
 
-def decode_split_bytes(Hkv, d, r, prefix, suffixes, n_agents, Hq, bls=True):
-    """Algorithmic bytes one decode split launch must move: the shared K and V
-    rows once per KV head, the low-rank rows (one shared plane, or one per
-    agent), each agent's own K/V/low-rank rows, and the queries."""
+def decode_split_bytes(Hkv, d, r, hidden, prefix, suffixes, n_agents, Hq, bls=True):
+    """Algorithmic bytes the split launch of one fused decode step must move:
+    the shared K and V rows once per KV head, the shared low-rank rows (one
+    plane, or one per agent), each agent's cached own K/V/low-rank rows, the
+    queries, and the step's appends (new K/V/low-rank rows written, x rows and
+    A read). suffixes are the own lengths before the step."""
     shared = 4 * Hkv * d * prefix + 2 * r * (prefix if bls else prefix * n_agents)
     own = sum(s * (4 * Hkv * d + 2 * r) for s in suffixes)
-    return shared + own + 2 * n_agents * Hq * d
+    append = n_agents * (4 * Hkv * d + 2 * r + 2 * hidden) + 2 * hidden * r
+    return shared + own + 2 * n_agents * Hq * d + append
 
 
 def prefill_flops(Hq, d, r, views, n_q):
@@ -144,7 +147,7 @@ def main():
     G = Hq // Hkv
     total_steps = args.warmup + args.steps
     prefill_n = 512
-    own_max = total_steps + (0 if args.no_prefill else prefill_n)
+    own_max = args.warmup + 2 * args.steps + (0 if args.no_prefill else prefill_n)
     max_pages = prefix // 64 + 1 + N * (own_max // 64 + 2) + 4
     c = dict(n_layers=L, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, hidden=hidden, rank=r,
              n_agents=N, mode=mode, page_size=64, max_pages=max_pages)
@@ -194,11 +197,11 @@ def main():
     S = [0] * N
 
     def step():
+        # one fused decode step per layer: append each agent's new row, attend
         for a in range(N):
-            sl[a] = S[a] + 1
+            sl[a] = S[a]
         for l in range(L):
-            B.skv_append_agents(ctx, l, ag, ones, kp[l], vp[l], xp[l], Ap)
-            B.skv_attn_decode(ctx, l, ag, bl, sl, qp[l], Bp, op[l])
+            B.skv_decode_step(ctx, l, ag, bl, sl, kp[l], vp[l], xp[l], Ap, qp[l], Bp, op[l])
         for a in range(N):
             S[a] += 1
 
@@ -207,27 +210,33 @@ def main():
     B.skv_sync(ctx)
     torch.cuda.synchronize()
 
-    # ---- timed region: K decode steps, with per-launch HIP events ----
-    suffix_hist = []
-    B.skv_set_timing(ctx, not args.no_events, ["decode_split"])
-    B.skv_collect_timing(ctx)
+    # ---- timed region: K decode steps (no events) -> value ----
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        suffix_hist.append(S[0] + 1)
         step()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    times = B.skv_collect_timing(ctx)
-    B.skv_set_timing(ctx, False)
-    wall = t1 - t0
+    wall = time.perf_counter() - t0
     ms_per_step = 1e3 * wall / args.steps
     value = N * args.steps / wall
 
-    split_ms, split_n = times["decode_split"]
-    bytes_avg = sum(decode_split_bytes(Hkv, d, r, prefix, [s] * N, N, Hq) for s in suffix_hist) / len(suffix_hist)
+    # ---- second timed region: the same steps with HIP events recorded by the
+    # dispatch of each split launch on the library's stream -> roofline ----
+    suffix_hist = []
+    times = {}
+    if not args.no_events:
+        B.skv_set_timing(ctx, True, ["decode_split", "decode_merge"])
+        B.skv_collect_timing(ctx)
+        for _ in range(args.steps):
+            suffix_hist.append(S[0])
+            step()
+        times = B.skv_collect_timing(ctx)
+        B.skv_set_timing(ctx, False)
+    split_ms, split_n = times.get("decode_split", (0.0, 0))
     roofline = None
     if split_n:
+        bytes_avg = sum(decode_split_bytes(Hkv, d, r, hidden, prefix, [s] * N, N, Hq)
+                        for s in suffix_hist) / len(suffix_hist)
         avg_split_s = split_ms / 1e3 / split_n
         achieved = bytes_avg / avg_split_s / 1e9
         traffic = load_traffic("decode_split_traffic.json")

@@ -155,6 +155,24 @@ int skv_attn_prefill(skv_ctx* ctx, int layer, int n, const int* agents, const in
 int skv_attn_decode(skv_ctx* ctx, int layer, int n, const int* agents, const int* base_len,
                     const int* suffix_len, const skv_bf16* q, const skv_bf16* B, skv_bf16* o);
 
+/* a2 + a3 + a5 + a6 fused for one decode token per listed agent: append the
+ * agent's new row (base K/V and its low-rank row X A, as skv_append_agents
+ * with counts of 1) at the end of its own suffix, then attend from that new
+ * position over SHARED[0:b_i] ++ OWN_i[0:S_i + 1] (as skv_attn_decode).
+ * Results equal the two separate calls up to fp32 summation order. On the
+ * GPU it is two launches: the split pass over the keys already cached plus
+ * the writes of the new rows, then the merge, which adds the new token as
+ * one more softmax term and applies B_i.
+ * base_len / suffix_len: b_i and S_i BEFORE the step (checked; each agent's
+ * own low-rank rows must be level with its base rows). k, v: device
+ * [n][Hkv][d]; x: device [n][hidden] or NULL (zero low-rank rows); A as in
+ * skv_append_agents; q, o: device [n][Hq][d]; B: device [N][r][Hkv*d].
+ * Errors: ARG, STATE, OOM (nothing is appended). */
+int skv_decode_step(skv_ctx* ctx, int layer, int n, const int* agents, const int* base_len,
+                    const int* suffix_len, const skv_bf16* k, const skv_bf16* v,
+                    const skv_bf16* x, const skv_bf16* A, const skv_bf16* q, const skv_bf16* B,
+                    skv_bf16* o);
+
 /* a7: set a view length on every layer (RoleKV "How we built it": crop at a
  * handoff; paperlayer Sec. 2: takeover boundary). Host metadata only.
  *   seq = agent i with no own rows and new_len >= b_i: (re)attach, b_i = new_len

@@ -76,6 +76,9 @@ int dev_init(Geometry& g);
 void dev_fini(Geometry& g);
 int dev_append(const Geometry& g, const AppendJob& job);
 int dev_attn_decode(const Geometry& g, const AttnJob& job);
+// Fused decode step: job holds lengths before the step; app appends one row
+// per agent (in the same order as job.ag).
+int dev_decode_step(const Geometry& g, const AttnJob& job, const AppendJob& app);
 int dev_attn_prefill(const Geometry& g, const AttnJob& job);
 int dev_sync(const Geometry& g);
 int dev_set_timing(Geometry& g, int mask);

@@ -21,6 +21,10 @@ int dev_attn_decode(const Geometry& g, const AttnJob&) {
   ++*g.launches;
   return SKV_OK;
 }
+int dev_decode_step(const Geometry& g, const AttnJob&, const AppendJob&) {
+  ++*g.launches;
+  return SKV_OK;
+}
 int dev_attn_prefill(const Geometry& g, const AttnJob&) {
   ++*g.launches;
   return SKV_OK;

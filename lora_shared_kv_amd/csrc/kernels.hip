@@ -31,6 +31,7 @@
 // which is exactly the B-operand slice P^T needs: P never leaves registers.
 // V and the low-rank rows are stored transposed in their pages ([d][slot] and
 // [rank][slot]) so their A-operand slices are 16 contiguous bytes.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -341,9 +342,9 @@ __device__ void append_lr_mfma_block(const AppendParams& p, int s, int tile, cha
   }
 }
 
-__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[64 * (128 + 8) * 2];
-  int b = blockIdx.x;
+// Work of block b of an append job (block 0 also writes the new page-table
+// entries). smem must hold at least 64 * (128 + 8) bf16.
+__device__ void append_block(const AppendParams& p, int b, char* smem) {
   if (b == 0 && p.update_tables) {
     for (int s = 0; s < p.n_spans; ++s) {
       const skv::Span& sp = p.spans[s];
@@ -369,6 +370,60 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     append_lr_dot_block(p, s, sub, smem);
   else
     append_lr_mfma_block(p, s, sub, smem);
+}
+
+__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[64 * (128 + 8) * 2];
+  append_block(p, blockIdx.x, smem);
+}
+
+// Block counts of an append job, per span: K/V tiles and low-rank blocks.
+void plan_append(const skv::Geometry& g, const skv::AppendJob& job, AppendParams& p) {
+  const uint64_t lay = (uint64_t)job.layer;
+  p.K = (u16*)(g.arena + g.k_off) + lay * g.k_layer();
+  p.VT = (u16*)(g.arena + g.vt_off) + lay * g.k_layer();
+  p.LRT = (u16*)(g.arena + g.lrt_off) + lay * g.lr_layer();
+  p.lr_plane = g.lr_plane();
+  p.tbl = (int32_t*)(g.arena + g.tbl_off) + lay * g.tbl_layer();
+  p.tbl_seq = (int)g.tbl_seq();
+  p.k = job.k;
+  p.v = job.v;
+  p.x = job.x;
+  p.Hkv = g.Hkv;
+  p.D = g.D;
+  p.r = g.r;
+  p.hidden = g.hidden;
+  p.do_kv = job.do_kv;
+  p.do_lr = job.do_lr;
+  p.update_tables = job.update_tables;
+  p.n_spans = job.n_spans;
+  memcpy(p.spans, job.spans, sizeof(skv::Span) * job.n_spans);
+  memcpy(p.ids, job.ids, sizeof(int32_t) * job.n_ids);
+  p.kv_block0[0] = 0;
+  p.lr_block0[0] = 0;
+  for (int s = 0; s < job.n_spans; ++s) {
+    const skv::Span& sp = job.spans[s];
+    p.kv_block0[s + 1] = p.kv_block0[s] + (job.do_kv ? sp.n_pages * g.Hkv : 0);
+    int nb = 0;
+    p.lr_kind[s] = 0;
+    if (job.do_lr) {
+      if (!job.x) {
+        p.lr_kind[s] = 0;
+        nb = sp.n_pages;
+      } else if (sp.n <= 8) {
+        p.lr_kind[s] = 1;
+        nb = sp.n;
+      } else {
+        p.lr_kind[s] = 2;
+        nb = (sp.n + kLrTile - 1) / kLrTile;
+      }
+    }
+    p.lr_block0[s + 1] = p.lr_block0[s] + nb;
+  }
+}
+
+int append_blocks(const AppendParams& p) {
+  return p.kv_block0[p.n_spans] + p.lr_block0[p.n_spans];
 }
 
 // ---------------------------------------------------------------------------
@@ -402,6 +457,8 @@ struct DecodeParams {
   int shared_len;                 // flattened length of the shared segment (max_b padded)
   int split, items_per_head;
   float scale_log2;
+  int n_app;        // leading blocks that append the step's new rows (fused decode step)
+  AppendParams app;
 };
 
 template <int D, int RB, int MB>
@@ -409,9 +466,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
   constexpr int KS = D / 32, DB = D / 16;
   __shared__ int32_t s_cpage[kMaxItemChunks];   // page id of each chunk of the item
   __shared__ int32_t s_ckey[kMaxItemChunks];    // (segment << 24) | first key of the chunk in its segment
-  extern __shared__ __attribute__((aligned(16))) float s_buf[];  // [2][RB*16][W]
+  extern __shared__ __attribute__((aligned(16))) float s_buf[];  // [4 or 2][RB*16][W]
 
-  const int item = blockIdx.x;
+  if ((int)blockIdx.x < p.n_app) {
+    // fused decode step: write the new K/V and low-rank rows; the items below
+    // read only keys cached before this step
+    append_block(p.app, blockIdx.x, reinterpret_cast<char*>(s_buf));
+    return;
+  }
+  const int item = blockIdx.x - p.n_app;
   const int g = item / p.items_per_head;
   const int j = item % p.items_per_head;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -574,9 +637,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     }
   }
 
-  // Combine the four waves: waves 2 and 3 park their states in LDS, waves 0
-  // and 1 fold them in, then every thread merges the two remaining states
-  // and writes the item's partial rows (o, o_lr, m, l) for the merge pass.
+  // Combine the four waves: with one row block every wave parks its state in
+  // LDS; with more, waves 2 and 3 park theirs and waves 0 and 1 fold them in.
+  // Then every thread merges the parked states and writes the item's partial
+  // rows (o, o_lr, m, l) for the merge pass.
   const int W = p.W;
   const int RP = RB * 16;
 #pragma unroll
@@ -619,23 +683,37 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
       }
     }
   };
-  if (w >= 2) park(s_buf + (w - 2) * RP * W, false);
-  __syncthreads();
-  if (w < 2) park(s_buf + w * RP * W, true);
-  __syncthreads();
+  constexpr int NB = RB == 1 ? 4 : 2;  // wave states left in LDS for the final merge
+  if (NB == 4) {
+    park(s_buf + w * RP * W, false);
+    __syncthreads();
+  } else {
+    if (w >= 2) park(s_buf + (w - 2) * RP * W, false);
+    __syncthreads();
+    if (w < 2) park(s_buf + w * RP * W, true);
+    __syncthreads();
+  }
   float* dst = p.part + (uint64_t)item * p.R * W;
-  const float* b0 = s_buf;
-  const float* b1 = s_buf + RP * W;
   const int E = D + p.r;
   for (int i = threadIdx.x; i < p.R * E; i += blockDim.x) {
     const int rho = i / E, e = i % E;
-    const float m0 = b0[rho * W + E], m1 = b1[rho * W + E];
-    const float mc = fmaxf(m0, m1);
-    const float a0 = __builtin_amdgcn_exp2f(m0 - mc), a1 = __builtin_amdgcn_exp2f(m1 - mc);
-    dst[rho * W + e] = a0 * b0[rho * W + e] + a1 * b1[rho * W + e];
+    float mb[NB], mc = -1e30f;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      mb[b] = s_buf[(b * RP + rho) * W + E];
+      mc = fmaxf(mc, mb[b]);
+    }
+    float acc = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float wt = __builtin_amdgcn_exp2f(mb[b] - mc);
+      acc += wt * s_buf[(b * RP + rho) * W + e];
+      lsum += wt * s_buf[(b * RP + rho) * W + E + 1];
+    }
+    dst[rho * W + e] = acc;
     if (e == 0) {
       dst[rho * W + E] = mc;
-      dst[rho * W + E + 1] = a0 * b0[rho * W + E + 1] + a1 * b1[rho * W + E + 1];
+      dst[rho * W + E + 1] = lsum;
     }
   }
 }
@@ -652,17 +730,32 @@ struct MergeParams {
   int n;
   int ag_id[SKV_MAX_AGENTS];
   int items_per_head;
+  // fused decode step: each agent's new token enters as one more softmax term
+  int step;
+  const u16* q;       // [n][Hq][D] of this group
+  const u16* k_new;   // [n][Hkv][D] of this group
+  const u16* v_new;   // [n][Hkv][D] of this group
+  const u16* LRT;     // layer base of plane 0 (holds the new low-rank rows)
+  uint64_t lr_plane;
+  int new_page[SKV_MAX_AGENTS], new_slot[SKV_MAX_AGENTS], plane[SKV_MAX_AGENTS];
+  float scale_log2;
 };
 
 // One workgroup per query row (agent, query head). Merges the row's partial
-// softmax states from every item of its KV head: M = max m_s, weights w_s = 2^(m_s - M)
-// / sum_s 2^(m_s - M) l_s, o = sum_s w_s o_s and o_lr = sum_s w_s o_lr,s; then
-// applies B_i once: o[d] += sum_k o_lr[k] B_i[k][g*D + d], rounded to bf16.
+// softmax states from every item of its KV head: M = max m_s, weights
+// w_s = 2^(m_s - M) / sum_s 2^(m_s - M) l_s, o = sum_s w_s o_s and
+// o_lr = sum_s w_s o_lr,s (a fused step adds the new token's own term);
+// then applies B_i once: o[d] += sum_k o_lr[k] B_i[k][g*D + d], in bf16.
+// Every global load the row needs is issued before the first reduction, so
+// the kernel waits on memory about once.
+constexpr int kMergeVec = 8;  // slots per thread held in registers
+
 __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
   __shared__ float s_w[kMaxMergeSlots];
   __shared__ f32x4 s_red[8][40];
   __shared__ float s_v[128 + 32];
-  __shared__ float s_m[4];
+  __shared__ float s_m[4], s_l[4];
+  __shared__ float s_new;
   const int row_id = blockIdx.x;
   const int hh = row_id % p.G;
   const int g = (row_id / p.G) % p.Hkv;
@@ -670,52 +763,89 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
   const int rho = a * p.G + hh;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n_slots = p.items_per_head;
+  const int E = p.D + p.r;
   auto slot_row = [&](int s) {
     return p.part + ((uint64_t)(g * p.items_per_head + s) * p.R + rho) * p.W;
   };
-  // weights
-  float M = -1e30f;
-  for (int s = threadIdx.x; s < n_slots; s += blockDim.x) {
-    const float m = slot_row(s)[p.D + p.r];
-    s_w[s] = m;
-    M = fmaxf(M, m);
+  // --- issue loads: per-slot (m, l), this thread's element quads, the new token
+  float m_s = -1e30f, l_s = 0.f;
+  if (threadIdx.x < n_slots) {
+    m_s = slot_row(threadIdx.x)[E];
+    l_s = slot_row(threadIdx.x)[E + 1];
   }
+  const int NQ = E / 4;
+  const int NG = min(8, (int)blockDim.x / NQ);
+  const int qd = threadIdx.x % NQ, sg = threadIdx.x / NQ;
+  const bool quad_thread = sg < NG;
+  f32x4 vals[kMergeVec];
+  int n_mine = 0;
+  if (quad_thread) {
+#pragma unroll
+    for (int i = 0; i < kMergeVec; ++i) {
+      const int s = sg + i * NG;
+      if (s < n_slots) {
+        vals[i] = *reinterpret_cast<const f32x4*>(slot_row(s) + 4 * qd);
+        n_mine = i + 1;
+      }
+    }
+  }
+  float dot = 0.f;
+  if (p.step && w == 0) {
+    const u16* qr = p.q + ((uint64_t)a * p.Hq + g * p.G + hh) * p.D;
+    const u16* kr = p.k_new + ((uint64_t)a * p.Hkv + g) * p.D;
+    for (int d = lane; d < p.D; d += 64) dot += bf2f(qr[d]) * bf2f(kr[d]);
+  }
+  float nv = 0.f;  // the new token's value for element threadIdx.x (v row, then low-rank row)
+  if (p.step && threadIdx.x < E) {
+    const int e = threadIdx.x;
+    nv = e < p.D ? bf2f(p.v_new[((uint64_t)a * p.Hkv + g) * p.D + e])
+                 : bf2f(p.LRT[(uint64_t)p.plane[a] * p.lr_plane + (uint64_t)p.new_page[a] * p.r * kPage +
+                              (e - p.D) * kPage + p.new_slot[a]]);
+  }
+  // --- softmax statistics
+  float M = m_s;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if (p.step && w == 0) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
+    if (lane == 0) s_new = dot * p.scale_log2;
+  }
   if (lane == 0) s_m[w] = M;
   __syncthreads();
-  M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
-  float L = 0.f;
-  for (int s = threadIdx.x; s < n_slots; s += blockDim.x) {
-    const float e = __builtin_amdgcn_exp2f(s_w[s] - M);
+  const float m_new = p.step ? s_new : -1e30f;
+  M = fmaxf(fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3])), m_new);
+  // slots beyond the first blockDim.x are folded in below through s_w
+  float e_s = threadIdx.x < n_slots ? __builtin_amdgcn_exp2f(m_s - M) : 0.f;
+  if (threadIdx.x < n_slots) s_w[threadIdx.x] = e_s;
+  float L = e_s * l_s;
+  for (int s = threadIdx.x + blockDim.x; s < n_slots; s += blockDim.x) {
+    const float e = __builtin_amdgcn_exp2f(slot_row(s)[E] - M);
     s_w[s] = e;
-    L += e * slot_row(s)[p.D + p.r + 1];
+    L += e * slot_row(s)[E + 1];
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+  if (lane == 0) s_l[w] = L;
   __syncthreads();
-  if (lane == 0) s_m[w] = L;
-  __syncthreads();
-  const float inv = 1.f / (s_m[0] + s_m[1] + s_m[2] + s_m[3]);
-  // weighted sums: element quads x slot groups
-  const int NQ = (p.D + p.r) / 4;
-  const int NG = min(8, (int)blockDim.x / NQ);
-  const int qd = threadIdx.x % NQ, sg = threadIdx.x / NQ;
-  if (sg < NG) {
+  const float e_new = p.step ? __builtin_amdgcn_exp2f(m_new - M) : 0.f;
+  const float inv = 1.f / (s_l[0] + s_l[1] + s_l[2] + s_l[3] + e_new);
+  // --- weighted sums: element quads x slot groups
+  if (quad_thread) {
     f32x4 acc = {0, 0, 0, 0};
-#pragma unroll 4
-    for (int s = sg; s < n_slots; s += NG) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(slot_row(s) + 4 * qd);
-      acc += s_w[s] * v;
-    }
+#pragma unroll
+    for (int i = 0; i < kMergeVec; ++i)
+      if (i < n_mine) acc += s_w[sg + i * NG] * vals[i];
+    for (int s = sg + kMergeVec * NG; s < n_slots; s += NG)
+      acc += s_w[s] * *reinterpret_cast<const f32x4*>(slot_row(s) + 4 * qd);
     s_red[sg][qd] = acc;
   }
   __syncthreads();
-  if (threadIdx.x < NQ) {
-    f32x4 acc = s_red[0][threadIdx.x];
-    for (int gg = 1; gg < NG; ++gg) acc += s_red[gg][threadIdx.x];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s_v[4 * threadIdx.x + j] = acc[j] * inv;
+  if (threadIdx.x < E) {
+    const int e = threadIdx.x;
+    float acc = 0.f;
+    for (int gg = 0; gg < NG; ++gg) acc += s_red[gg][e / 4][e % 4];
+    s_v[e] = (acc + e_new * nv) * inv;
   }
   __syncthreads();
   const int HD = p.Hkv * p.D;
@@ -945,32 +1075,33 @@ struct DevState {
   }
 };
 
-struct TimedLaunch {
-  DevState* st;
-  hipStream_t stream;
-  int kind;
+// Launch on the context stream. When timing is on for this kernel kind the
+// dispatch itself records start/stop events (hipExtLaunchKernelGGL), so the
+// measured interval is the kernel's own execution.
+template <typename Kernel, typename Params>
+int launch(const skv::Geometry& g, int kind, Kernel kernel, dim3 grid, size_t lds,
+           const Params& params, const char* what) {
+  auto* st = (DevState*)g.dev;
+  hipStream_t stream = (hipStream_t)g.stream;
   hipEvent_t a = nullptr, b = nullptr;
-  TimedLaunch(const skv::Geometry& g, int k)
-      : st((DevState*)g.dev), stream((hipStream_t)g.stream), kind(k) {
-    if (st && (st->timing >> k & 1)) {
-      a = st->get();
-      b = st->get();
-      if (a && b) (void)hipEventRecord(a, stream);
-    }
+  if (st && (st->timing >> kind & 1)) {
+    a = st->get();
+    b = st->get();
   }
-  int done(const char* what) {
-    hipError_t e = hipGetLastError();
-    if (a && b) {
-      (void)hipEventRecord(b, stream);
-      st->recs.push_back({kind, a, b});
-    }
-    if (e != hipSuccess) {
-      set_err(what, e);
-      return SKV_ERR_HIP;
-    }
-    return SKV_OK;
+  if (a && b) {
+    hipExtLaunchKernelGGL(kernel, grid, dim3(256), (uint32_t)lds, stream, a, b, 0, params);
+    st->recs.push_back({kind, a, b});
+  } else {
+    hipLaunchKernelGGL(kernel, grid, dim3(256), lds, stream, params);
   }
-};
+  ++*g.launches;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_err(what, e);
+    return SKV_ERR_HIP;
+  }
+  return SKV_OK;
+}
 
 int decode_group_limit(const skv::Geometry& g) {
   // agents per decode launch: rows <= 64, stacked low-rank rows <= 128,
@@ -989,24 +1120,26 @@ int decode_group_limit(const skv::Geometry& g) {
 int w_of(const skv::Geometry& g) { return g.D + g.r + 4; }
 
 template <int D, int RB, int MB>
-void launch_split_t(const DecodeParams& p, int items, hipStream_t st) {
-  size_t lds = (size_t)2 * RB * 16 * p.W * sizeof(float);
-  hipLaunchKernelGGL((decode_split_kernel<D, RB, MB>), dim3(items), dim3(256), lds, st, p);
+int launch_split_t(const skv::Geometry& g, const DecodeParams& p, int items) {
+  size_t lds = (size_t)(RB == 1 ? 4 : 2) * RB * 16 * p.W * sizeof(float);
+  if (p.n_app > 0) lds = std::max(lds, (size_t)64 * (128 + 8) * 2);  // append blocks' staging
+  return launch(g, 2, decode_split_kernel<D, RB, MB>, dim3(p.n_app + items), lds, p,
+                "decode_split_kernel");
 }
 
 template <int D>
-bool launch_split_d(int rb, int mb, const DecodeParams& p, int items, hipStream_t st) {
-  if (rb == 1 && mb == 1) launch_split_t<D, 1, 1>(p, items, st);
-  else if (rb == 1 && mb == 2) launch_split_t<D, 1, 2>(p, items, st);
-  else if (rb == 1 && mb == 4) launch_split_t<D, 1, 4>(p, items, st);
-  else if (rb == 1 && mb == 8) launch_split_t<D, 1, 8>(p, items, st);
-  else if (rb == 2 && mb == 1) launch_split_t<D, 2, 1>(p, items, st);
-  else if (rb == 2 && mb == 2) launch_split_t<D, 2, 2>(p, items, st);
-  else if (rb == 2 && mb == 4) launch_split_t<D, 2, 4>(p, items, st);
-  else if (rb == 4 && mb == 1) launch_split_t<D, 4, 1>(p, items, st);
-  else if (rb == 4 && mb == 2) launch_split_t<D, 4, 2>(p, items, st);
-  else return false;
-  return true;
+int launch_split_d(const skv::Geometry& g, int rb, int mb, const DecodeParams& p, int items) {
+  if (rb == 1 && mb == 1) return launch_split_t<D, 1, 1>(g, p, items);
+  if (rb == 1 && mb == 2) return launch_split_t<D, 1, 2>(g, p, items);
+  if (rb == 1 && mb == 4) return launch_split_t<D, 1, 4>(g, p, items);
+  if (rb == 1 && mb == 8) return launch_split_t<D, 1, 8>(g, p, items);
+  if (rb == 2 && mb == 1) return launch_split_t<D, 2, 1>(g, p, items);
+  if (rb == 2 && mb == 2) return launch_split_t<D, 2, 2>(g, p, items);
+  if (rb == 2 && mb == 4) return launch_split_t<D, 2, 4>(g, p, items);
+  if (rb == 4 && mb == 1) return launch_split_t<D, 4, 1>(g, p, items);
+  if (rb == 4 && mb == 2) return launch_split_t<D, 4, 2>(g, p, items);
+  snprintf(g_err, sizeof g_err, "no decode kernel for rb=%d mb=%d", rb, mb);
+  return SKV_ERR_UNSUPPORTED;
 }
 
 }  // namespace
@@ -1051,57 +1184,16 @@ void dev_fini(Geometry& g) {
 
 int dev_append(const Geometry& g, const AppendJob& job) {
   AppendParams p{};
-  const uint64_t lay = (uint64_t)job.layer;
-  p.K = (u16*)(g.arena + g.k_off) + lay * g.k_layer();
-  p.VT = (u16*)(g.arena + g.vt_off) + lay * g.k_layer();
-  p.LRT = (u16*)(g.arena + g.lrt_off) + lay * g.lr_layer();
-  p.lr_plane = g.lr_plane();
-  p.tbl = (int32_t*)(g.arena + g.tbl_off) + lay * g.tbl_layer();
-  p.tbl_seq = (int)g.tbl_seq();
-  p.k = job.k;
-  p.v = job.v;
-  p.x = job.x;
-  p.Hkv = g.Hkv;
-  p.D = g.D;
-  p.r = g.r;
-  p.hidden = g.hidden;
-  p.do_kv = job.do_kv;
-  p.do_lr = job.do_lr;
-  p.update_tables = job.update_tables;
-  p.n_spans = job.n_spans;
-  memcpy(p.spans, job.spans, sizeof(Span) * job.n_spans);
-  memcpy(p.ids, job.ids, sizeof(int32_t) * job.n_ids);
-  p.kv_block0[0] = 0;
-  p.lr_block0[0] = 0;
-  for (int s = 0; s < job.n_spans; ++s) {
-    const Span& sp = job.spans[s];
-    p.kv_block0[s + 1] = p.kv_block0[s] + (job.do_kv ? sp.n_pages * g.Hkv : 0);
-    int nb = 0;
-    p.lr_kind[s] = 0;
-    if (job.do_lr) {
-      if (!job.x) {
-        p.lr_kind[s] = 0;
-        nb = sp.n_pages;
-      } else if (sp.n <= 8) {
-        p.lr_kind[s] = 1;
-        nb = sp.n;
-      } else {
-        p.lr_kind[s] = 2;
-        nb = (sp.n + kLrTile - 1) / kLrTile;
-      }
-    }
-    p.lr_block0[s + 1] = p.lr_block0[s] + nb;
-  }
-  const int blocks = p.kv_block0[job.n_spans] + p.lr_block0[job.n_spans];
+  plan_append(g, job, p);
+  const int blocks = append_blocks(p);
   if (blocks == 0 && !job.update_tables) return SKV_OK;
-  TimedLaunch t(g, job.do_kv ? 0 : 1);
-  hipLaunchKernelGGL(append_kernel, dim3(std::max(blocks, 1)), dim3(256), 0,
-                     (hipStream_t)g.stream, p);
-  ++*g.launches;
-  return t.done("append_kernel");
+  return launch(g, job.do_kv ? 0 : 1, append_kernel, dim3(std::max(blocks, 1)), 0, p, "append_kernel");
 }
 
-int dev_attn_decode(const Geometry& g, const AttnJob& job) {
+// Decode for the agents of job, in groups that fit one launch. With app (a
+// fused decode step) each group's split launch also writes the group's new
+// rows and the merge adds the new tokens.
+static int decode_impl(const Geometry& g, const AttnJob& job, const AppendJob* app) {
   const int ng = decode_group_limit(g);
   hipStream_t st = (hipStream_t)g.stream;
   const int W = w_of(g);
@@ -1151,9 +1243,9 @@ int dev_attn_decode(const Geometry& g, const AttnJob& job) {
     // items: about one per CU over all KV heads, in whole 32-key chunks
     const int chunks = total / 32;
     int per_head = std::max(1, std::min(chunks, kCUs / g.Hkv));
-    int split = (chunks + per_head - 1) / per_head * 32;
+    int split = std::max(32, (chunks + per_head - 1) / per_head * 32);
     if (split > kMaxItemChunks * 32) split = kMaxItemChunks * 32;
-    const int items_per_head = (total + split - 1) / split;
+    const int items_per_head = (total + split - 1) / split;  // 0 when nothing is cached yet
     if ((uint64_t)items_per_head * g.Hkv > (uint64_t)kMaxItems || items_per_head > kMaxMergeSlots) {
       snprintf(g_err, sizeof g_err, "decode view too long for the split plan (%d keys)", total);
       return SKV_ERR_UNSUPPORTED;
@@ -1166,18 +1258,28 @@ int dev_attn_decode(const Geometry& g, const AttnJob& job) {
     int mb = (p.n_planes * g.r + 15) / 16;
     mb = mb <= 1 ? 1 : (mb <= 2 ? 2 : (mb <= 4 ? 4 : 8));
     const int items = items_per_head * g.Hkv;
-    {
-      TimedLaunch t(g, 2);
-      bool ok = g.D == 128 ? launch_split_d<128>(rb, mb, p, items, st)
-                           : launch_split_d<64>(rb, mb, p, items, st);
-      if (!ok) {
-        snprintf(g_err, sizeof g_err, "no decode kernel for rb=%d mb=%d", rb, mb);
-        return SKV_ERR_UNSUPPORTED;
+    if (app) {
+      AppendJob sub{};
+      sub.layer = app->layer;
+      sub.do_kv = app->do_kv;
+      sub.do_lr = app->do_lr;
+      sub.update_tables = app->update_tables;
+      sub.k = app->k;
+      sub.v = app->v;
+      sub.x = app->x;
+      for (int i = 0; i < n; ++i) {
+        Span sp = app->spans[a0 + i];
+        for (int t = 0; t < sp.n_pages; ++t) sub.ids[sub.n_ids + t] = app->ids[sp.ids_off + t];
+        sp.ids_off = sub.n_ids;
+        sub.n_ids += sp.n_pages;
+        sub.spans[sub.n_spans++] = sp;
       }
-      ++*g.launches;
-      int rc = t.done("decode_split_kernel");
-      if (rc != SKV_OK) return rc;
+      plan_append(g, sub, p.app);
+      p.n_app = append_blocks(p.app);
+      if (p.n_app == 0) p.n_app = 1;  // the table update rides on block 0
     }
+    int rc = g.D == 128 ? launch_split_d<128>(g, rb, mb, p, items) : launch_split_d<64>(g, rb, mb, p, items);
+    if (rc != SKV_OK) return rc;
     MergeParams mp{};
     mp.part = part;
     mp.B = job.B;
@@ -1192,15 +1294,36 @@ int dev_attn_decode(const Geometry& g, const AttnJob& job) {
     mp.n = n;
     for (int i = 0; i < n; ++i) mp.ag_id[i] = p.ag_id[i];
     mp.items_per_head = items_per_head;
-    {
-      TimedLaunch t(g, 3);
-      hipLaunchKernelGGL(decode_merge_kernel, dim3(n * g.Hkv * g.G), dim3(256), 0, st, mp);
-      ++*g.launches;
-      int rc = t.done("decode_merge_kernel");
-      if (rc != SKV_OK) return rc;
+    if (app) {
+      mp.step = 1;
+      mp.q = p.q;
+      mp.k_new = app->k + (uint64_t)a0 * g.Hkv * g.D;
+      mp.v_new = app->v + (uint64_t)a0 * g.Hkv * g.D;
+      mp.LRT = p.LRT;
+      mp.lr_plane = g.lr_plane();
+      for (int i = 0; i < n; ++i) {
+        const Span& sp = app->spans[a0 + i];
+        mp.new_page[i] = app->ids[sp.ids_off];
+        mp.new_slot[i] = sp.pos0 % kPage;
+        mp.plane[i] = sp.plane;
+      }
+      mp.scale_log2 = p.scale_log2;
     }
+    rc = launch(g, 3, decode_merge_kernel, dim3(n * g.Hkv * g.G), 0, mp, "decode_merge_kernel");
+    if (rc != SKV_OK) return rc;
   }
   return SKV_OK;
+}
+
+static_assert(sizeof(DecodeParams) <= 4096, "kernel arguments too large");
+static_assert(sizeof(MergeParams) <= 4096, "kernel arguments too large");
+static_assert(sizeof(AppendParams) <= 4096, "kernel arguments too large");
+static_assert(sizeof(PrefillParams) <= 4096, "kernel arguments too large");
+
+int dev_attn_decode(const Geometry& g, const AttnJob& job) { return decode_impl(g, job, nullptr); }
+
+int dev_decode_step(const Geometry& g, const AttnJob& job, const AppendJob& app) {
+  return decode_impl(g, job, &app);
 }
 
 int dev_attn_prefill(const Geometry& g, const AttnJob& job) {
@@ -1237,18 +1360,12 @@ int dev_attn_prefill(const Geometry& g, const AttnJob& job) {
   }
   p.scale_log2 = 1.4426950408889634f / sqrtf((float)g.D);
   const int blocks = p.blk0[job.n] * g.Hkv;
-  hipStream_t st = (hipStream_t)g.stream;
-  TimedLaunch t(g, 4);
   const int mb = (g.r + 15) / 16;
-  if (g.D == 128) {
-    if (mb == 1) hipLaunchKernelGGL((prefill_kernel<128, 1>), dim3(blocks), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((prefill_kernel<128, 2>), dim3(blocks), dim3(256), 0, st, p);
-  } else {
-    if (mb == 1) hipLaunchKernelGGL((prefill_kernel<64, 1>), dim3(blocks), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((prefill_kernel<64, 2>), dim3(blocks), dim3(256), 0, st, p);
-  }
-  ++*g.launches;
-  return t.done("prefill_kernel");
+  if (g.D == 128)
+    return mb == 1 ? launch(g, 4, prefill_kernel<128, 1>, dim3(blocks), 0, p, "prefill_kernel")
+                   : launch(g, 4, prefill_kernel<128, 2>, dim3(blocks), 0, p, "prefill_kernel");
+  return mb == 1 ? launch(g, 4, prefill_kernel<64, 1>, dim3(blocks), 0, p, "prefill_kernel")
+                 : launch(g, 4, prefill_kernel<64, 2>, dim3(blocks), 0, p, "prefill_kernel");
 }
 
 int dev_sync(const Geometry& g) {

@@ -445,6 +445,102 @@ int skv_attn_decode(skv_ctx* c, int layer, int n, const int* agents, const int* 
   return SKV_OK;
 }
 
+int skv_decode_step(skv_ctx* c, int layer, int n, const int* agents, const int* base_len,
+                    const int* suffix_len, const skv_bf16* k, const skv_bf16* v,
+                    const skv_bf16* x, const skv_bf16* A, const skv_bf16* q, const skv_bf16* B,
+                    skv_bf16* o) {
+  if (!c) return SKV_ERR_ARG;
+  const Geometry& g = c->g;
+  if (layer < 0 || layer >= g.L) return c->fail(SKV_ERR_ARG, "layer %d out of range", layer);
+  if (n < 1 || n > g.N) return c->fail(SKV_ERR_ARG, "agent count %d", n);
+  if (!agents || !base_len || !suffix_len || !k || !v || !q || !B || !o)
+    return c->fail(SKV_ERR_ARG, "null argument");
+  if (x && !A) return c->fail(SKV_ERR_ARG, "x given without A");
+  Layer& l = c->layers[layer];
+  uint32_t seen = 0;
+  for (int i = 0; i < n; ++i) {
+    int a = agents[i];
+    if (a < 0 || a >= g.N || (seen >> a & 1u)) return c->fail(SKV_ERR_ARG, "agent list entry %d", a);
+    seen |= 1u << a;
+  }
+  AttnJob job{};
+  job.layer = layer;
+  job.n = n;
+  int need = 0;
+  for (int i = 0; i < n; ++i) {
+    int a = agents[i];
+    int b = c->base_len[a], S = l.len[1 + a];
+    if (base_len[i] != b || suffix_len[i] != S)
+      return c->fail(SKV_ERR_STATE,
+                     "agent %d: caller lengths (b=%d, S=%d) differ from the cache (b=%d, S=%d)", a,
+                     base_len[i], suffix_len[i], b, S);
+    int p = c->plane_of(a);
+    if (l.lr_own[a] != S)
+      return c->fail(SKV_ERR_STATE, "agent %d low-rank rows (%d) lag base rows (%d)", a, l.lr_own[a], S);
+    if (l.lr_shared[p] < b)
+      return c->fail(SKV_ERR_STATE, "agent %d: low-rank rows do not cover the view", a);
+    job.ag[i] = skv::AttnAgent{a, b, S, p, 1, i};
+    need += ceil_div(S + 1, g.ps) - (int)l.tbl[1 + a].size();
+  }
+  if (need > (int)l.free.size())
+    return c->fail(SKV_ERR_OOM, "layer %d: %d pages needed, %d free", layer, need, (int)l.free.size());
+  std::vector<std::vector<int32_t>> tables(n);
+  std::vector<int32_t> taken;
+  for (int i = 0; i < n; ++i) {
+    int slot = 1 + agents[i];
+    tables[i] = l.tbl[slot];
+    if (ceil_div(l.len[slot] + 1, g.ps) > (int)tables[i].size()) {
+      int32_t id = *l.free.begin();
+      l.free.erase(l.free.begin());
+      tables[i].push_back(id);
+      taken.push_back(id);
+    }
+  }
+  AppendJob app{};
+  app.layer = layer;
+  app.do_kv = true;
+  app.do_lr = true;
+  app.update_tables = true;
+  app.k = k;
+  app.v = v;
+  app.x = x;
+  const uint64_t a_stride = (uint64_t)g.hidden * g.r;
+  for (int i = 0; i < n; ++i) {
+    int a = agents[i];
+    const int pos = l.len[1 + a];
+    Span sp{};
+    sp.seq_slot = 1 + a;
+    sp.pos0 = pos;
+    sp.n = 1;
+    sp.src_row = i;
+    sp.first_page = pos / g.ps;
+    sp.n_pages = 1;
+    sp.ids_off = app.n_ids;
+    sp.plane = c->plane_of(a);
+    sp.a = x ? (g.mode == SKV_BASE_SHARED ? A + a_stride * a : A) : nullptr;
+    app.ids[app.n_ids++] = tables[i][sp.first_page];
+    app.spans[app.n_spans++] = sp;
+  }
+  job.q = q;
+  job.B = B;
+  job.o = o;
+  int rc = skv::dev_decode_step(g, job, app);
+  if (rc != SKV_OK) {
+    for (int32_t p : taken) l.free.insert(p);
+    return c->fail(rc, "device decode step failed: %s", skv::dev_last_error());
+  }
+  for (int i = 0; i < n; ++i) {
+    int slot = 1 + agents[i];
+    l.tbl[slot] = std::move(tables[i]);
+    l.len[slot] += 1;
+    l.lr_own[agents[i]] += 1;
+  }
+  c->counters.pages_alloc += (int64_t)taken.size();
+  c->counters.base_rows_own += n;
+  (x ? c->counters.lr_rows : c->counters.lr_zero_rows) += n;
+  return SKV_OK;
+}
+
 int skv_crop(skv_ctx* c, int seq, int new_len) {
   if (!c) return SKV_ERR_ARG;
   if (!c->seq_ok(seq)) return c->fail(SKV_ERR_ARG, "sequence %d out of range", seq);

@@ -59,6 +59,7 @@ EXPORTS = {
     "skv_append_agents": (_I, [_P, _I, _I, _IP, _IP, _P, _P, _P, _P]),
     "skv_attn_prefill": (_I, [_P, _I, _I, _IP, _IP, _IP, _IP, _P, _P, _P]),
     "skv_attn_decode": (_I, [_P, _I, _I, _IP, _IP, _IP, _P, _P, _P]),
+    "skv_decode_step": (_I, [_P, _I, _I, _IP, _IP, _IP, _P, _P, _P, _P, _P, _P, _P]),
     "skv_crop": (_I, [_P, _I, _I]),
     "skv_get_lens": (_I, [_P, _I, _IP, _IP, _IP, _IP, _IP]),
     "skv_get_pages": (_I, [_P, _I, _I, ctypes.POINTER(ctypes.c_int32), _I]),
@@ -243,6 +244,18 @@ def skv_attn_decode(ctx: Ctx, layer: int, agents, base_len, suffix_len, q, B, o)
     qs = (n, ctx.Hq, ctx.d)
     ctx._check(ctx.lib.skv_attn_decode(ctx.handle, layer, n, ag, bl, sl, _ptr(q, qs, "q"),
                                        _ptr(B, ctx.b_shape, "B"), _ptr(o, qs, "o")))
+
+
+def skv_decode_step(ctx: Ctx, layer: int, agents, base_len, suffix_len, k, v, x, A, q, B, o):
+    ag, n = _ints(agents)
+    bl, _ = _ints(base_len)
+    sl, _ = _ints(suffix_len)
+    kv = (n, ctx.Hkv, ctx.d)
+    qs = (n, ctx.Hq, ctx.d)
+    ctx._check(ctx.lib.skv_decode_step(
+        ctx.handle, layer, n, ag, bl, sl, _ptr(k, kv, "k"), _ptr(v, kv, "v"),
+        _ptr(x, (n, ctx.hidden), "x"), _ptr(A, ctx.a_shape, "A"), _ptr(q, qs, "q"),
+        _ptr(B, ctx.b_shape, "B"), _ptr(o, qs, "o")))
 
 
 def skv_crop(ctx: Ctx, seq: int, new_len: int):

@@ -160,6 +160,29 @@ class Attend:
     tag: str = ""
 
 
+@dataclass
+class DecodeStep:
+    """One decode token per listed agent: append its row, then attend from it.
+    base_len / suffix_len are the lengths before the step."""
+    layer: int
+    agents: List[int]
+    base_len: List[int]
+    suffix_len: List[int]
+    k: np.ndarray          # [n][Hkv][d]
+    v: np.ndarray
+    x: Optional[np.ndarray]   # [n][hidden] or None (zero low-rank rows)
+    a: Optional[np.ndarray]   # as AppendAgents.a
+    q: np.ndarray          # [n][Hq][d]
+    b: np.ndarray          # [n_agents][r][Hkv*d]
+    tag: str = ""
+
+    @property
+    def n_q(self):
+        return [1] * len(self.agents)
+
+    kind = "step"
+
+
 # ---------------------------------------------------------------------------
 # Schedule builder: keeps the lengths each attention call must carry.
 # ---------------------------------------------------------------------------
@@ -275,6 +298,21 @@ class Schedule:
         for ag, c in zip(agents, counts):
             self.S[layer][ag] += c
 
+    def decode_step(self, layer: int, agents: Sequence[int], lr: str = "x", tag=""):
+        """Fused decode step: one new row per agent, then attention from it."""
+        s = self.s
+        n = len(agents)
+        k, v = self._kv(n)
+        x = self.d.normal((n, s.hidden)) if lr == "x" else None
+        q = self._q(n)
+        ev = DecodeStep(layer, list(agents), [self.b[a] for a in agents],
+                        [self.S[layer][a] for a in agents], k, v, x,
+                        None if x is None else self.A[layer], q, self.B[layer], tag)
+        self.events.append(ev)
+        for a in agents:
+            self.S[layer][a] += 1
+        return ev
+
     def attend(self, kind: str, layer: int, agents: Sequence[int], n_q: Sequence[int], tag=""):
         q = self._q(int(sum(n_q)))
         ev = Attend(kind, layer, list(agents), [self.b[a] for a in agents],
@@ -288,7 +326,7 @@ class Schedule:
 # ---------------------------------------------------------------------------
 
 
-def tiny_schedule(seed=1000, n_layers=None, decode_steps=16, prefill=32, **kw) -> Schedule:
+def tiny_schedule(seed=1000, n_layers=None, decode_steps=16, prefill=32, fused=False, **kw) -> Schedule:
     """Tiny: shared prefix 1024, two agents, 32-token suffix prefill each, then decodes."""
     s = TINY
     sc = Schedule(s, seed, n_layers, **kw)
@@ -303,8 +341,11 @@ def tiny_schedule(seed=1000, n_layers=None, decode_steps=16, prefill=32, **kw) -
     agents = list(range(s.n_agents))
     for t in range(decode_steps):
         for l in range(sc.L):
-            sc.own_rows(l, agents, [1] * len(agents))
-            sc.attend("decode", l, agents, [1] * len(agents), tag=f"decode t{t}")
+            if fused:
+                sc.decode_step(l, agents, tag=f"step t{t}")
+            else:
+                sc.own_rows(l, agents, [1] * len(agents))
+                sc.attend("decode", l, agents, [1] * len(agents), tag=f"decode t{t}")
     return sc
 
 
@@ -360,7 +401,7 @@ def qwen3_schedule(takeover=160, seed=1002, n_layers=1, decode=64, **kw) -> Sche
     return sc
 
 
-def llama3_schedule(prefix=33792, seed=1003, n_layers=1, decode=256, **kw) -> Schedule:
+def llama3_schedule(prefix=33792, seed=1003, n_layers=1, decode=256, fused=False, **kw) -> Schedule:
     """Shared-A agents decode one token each per step over a long shared trajectory."""
     s = LLAMA3.with_(prefix=prefix)
     sc = Schedule(s, seed, n_layers, **kw)
@@ -371,8 +412,11 @@ def llama3_schedule(prefix=33792, seed=1003, n_layers=1, decode=256, **kw) -> Sc
         sc.attach(a)
     for t in range(decode):
         for l in range(sc.L):
-            sc.own_rows(l, agents, [1] * len(agents))
-            sc.attend("decode", l, agents, [1] * len(agents), tag=f"decode t{t}")
+            if fused:
+                sc.decode_step(l, agents, tag=f"step t{t}")
+            else:
+                sc.own_rows(l, agents, [1] * len(agents))
+                sc.attend("decode", l, agents, [1] * len(agents), tag=f"decode t{t}")
     return sc
 
 

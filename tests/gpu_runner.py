@@ -12,7 +12,7 @@ import numpy as np
 import torch
 
 from lora_shared_kv_amd import skv as B
-from synth import (AppendAgents, AppendBase, AppendLowrank, Attend, Crop, Schedule,
+from synth import (AppendAgents, AppendBase, AppendLowrank, Attend, Crop, DecodeStep, Schedule,
                    bf16_bits_to_f64)
 from oracle.run import apply_event, model_for
 
@@ -44,6 +44,9 @@ def pages_needed(sc: Schedule, slack=8):
         elif isinstance(ev, AppendAgents):
             for a, c in zip(ev.agents, ev.counts):
                 cur[(ev.layer, a)] = cur.get((ev.layer, a), 0) + c
+        elif isinstance(ev, DecodeStep):
+            for a in ev.agents:
+                cur[(ev.layer, a)] = cur.get((ev.layer, a), 0) + 1
         elif isinstance(ev, Crop):
             pass
         for l in range(sc.L):
@@ -82,6 +85,12 @@ class GpuRun:
                                 dev(ev.a))
         elif isinstance(ev, Crop):
             B.skv_crop(c, ev.seq, ev.new_len)
+        elif isinstance(ev, DecodeStep):
+            q = dev(ev.q)
+            o = torch.empty_like(q)
+            B.skv_decode_step(c, ev.layer, ev.agents, ev.base_len, ev.suffix_len, dev(ev.k),
+                              dev(ev.v), dev(ev.x), dev(ev.a), q, self.b_dev(ev), o)
+            return o
         elif isinstance(ev, Attend):
             q = dev(ev.q)
             o = torch.empty_like(q)

@@ -55,6 +55,69 @@ def mini(shape, prefix, own, decode_steps=2, seed=7, attach=None, nq_extra=0, pe
 # the five workloads
 # --------------------------------------------------------------------------
 
+def test_tiny_fused_decode_steps():
+    R = _runner()
+    sc = synth.tiny_schedule(fused=True)
+    _, _, res = R.run_parity(sc, log=log)
+    assert len(res) == 2 + 16
+
+
+@pytest.mark.parametrize("prefix,steps", [(33792, 3), (32768, 70)])
+def test_llama3_fused_decode_steps(prefix, steps):
+    # 70 steps from a page-aligned prefix cross into a second own page
+    R = _runner()
+    sc = synth.llama3_schedule(prefix=prefix, decode=steps, fused=True)
+    R.run_parity(sc, log=log)
+
+
+def test_fused_step_edge_cases():
+    """Empty view (the first token is the whole view), zero low-rank rows,
+    agents at different boundaries, groups larger than one launch."""
+    R = _runner()
+    for shape, prefix, attach in [
+        (Shape("e", 1, 8, 2, 128, 256, 8, 3, BASE_SHARED, 0), 0, [0, 0, 0]),
+        (Shape("e", 1, 8, 2, 64, 256, 16, 3, BASE_SHARED, 0), 200, [200, 131, 64]),
+        (Shape("e", 1, 16, 4, 64, 256, 8, 16, BASE_LR_SHARED, 0), 90, None),
+    ]:
+        sc = Schedule(shape, 11, n_layers=1)
+        sc.draw_adapters()
+        if prefix:
+            sc.shared_prefix(prefix)
+        agents = list(range(shape.n_agents))
+        for a in agents:
+            sc.attach(a, attach[a] if attach else prefix)
+        for t in range(3):
+            sc.decode_step(0, agents, lr="zero" if t == 1 else "x", tag=f"step{t}")
+        R.run_parity(sc, log=log)
+
+
+def test_fused_step_cache_matches_separate_calls():
+    """The fused step leaves the same cache bytes as append + decode."""
+    import torch
+    R = _runner()
+    shape = Shape("e", 1, 16, 4, 128, 512, 16, 3, BASE_SHARED, 0)
+    runs = []
+    for fused in (False, True):
+        sc = Schedule(shape, 5, n_layers=1)
+        sc.draw_adapters()
+        sc.shared_prefix(300)
+        for a in range(3):
+            sc.attach(a)
+        for t in range(70):
+            if fused:
+                sc.decode_step(0, [0, 1, 2])
+            else:
+                sc.own_rows(0, [0, 1, 2], [1, 1, 1])
+                sc.attend("decode", 0, [0, 1, 2], [1, 1, 1])
+        gpu, orc, _ = R.run_parity(sc)
+        runs.append([t.cpu().numpy() for t in _pool_views(gpu)])
+    k0, v0, l0 = runs[0]
+    k1, v1, l1 = runs[1]
+    assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
+    d = np.abs(l0.view(np.uint16).astype(np.int32) - l1.view(np.uint16).astype(np.int32))
+    assert d.max() <= 1     # low-rank rows: fp32 sums in a different order, at most 1 bf16 ulp
+
+
 def test_tiny_full_schedule():
     R = _runner()
     sc = synth.tiny_schedule()

@@ -64,6 +64,8 @@ op = st.one_of(
     st.tuples(st.just("crop"), st.integers(-1, 2), st.integers(-1, 16)),
     st.tuples(st.just("attend"), st.integers(0, 1), st.lists(st.integers(0, 2), min_size=1, max_size=3),
               st.integers(0, 2), st.integers(1, 3)),
+    st.tuples(st.just("step"), st.integers(0, 1), st.lists(st.integers(0, 2), min_size=1, max_size=3,
+                                                            unique=True), st.booleans()),
 )
 
 
@@ -120,6 +122,21 @@ def test_random_ops_match_the_oracle(ops, mode):
             want = _oracle_rc(orc.crop, seq, n)
             try:
                 B.skv_crop(ctx, seq, n); got = "OK"
+            except B.SkvError as e:
+                got = e.code
+        elif kind == "step":
+            from oracle.run import decode_step
+            _, layer, agents, with_x = o
+            bl = [orc.base_len[a] for a in agents]
+            sl = [orc.length[layer][a] for a in agents]
+            n = len(agents)
+            z = np.zeros((n, Hkv, d))
+            x = np.zeros((n, hidden)) if with_x else None
+            a = (np.zeros((cfg["n_agents"], hidden, r)) if mode == 0 else np.zeros((hidden, r))) if with_x else None
+            want = _oracle_rc(decode_step, orc, layer, agents, bl, sl, z, z, x, a)
+            try:
+                B.skv_decode_step(ctx, layer, agents, bl, sl, FAKE, FAKE, FAKE if with_x else None,
+                                  FAKE if with_x else None, FAKE, FAKE, FAKE); got = "OK"
             except B.SkvError as e:
                 got = e.code
         else:
