@@ -455,9 +455,10 @@ struct DecodeParams {
   int planes[SKV_MAX_AGENTS];     // stacked low-rank planes of this group
   int seg_off[SKV_MAX_AGENTS + 1];  // flattened offset of each own suffix; seg_off[n] = total
   int shared_len;                 // flattened length of the shared segment (max_b padded)
-  int split, items_per_head;
+  int head_chunks;     // C: 32-key chunks of one head's flattened sequence
+  int items_per_head;  // I: item j takes chunks [j C / I, (j + 1) C / I)
   float scale_log2;
-  int n_app;        // leading blocks that append the step's new rows (fused decode step)
+  int n_app;        // leading blocks that write the step's low-rank rows and table entries
   AppendParams app;
 };
 
@@ -469,8 +470,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
   extern __shared__ __attribute__((aligned(16))) float s_buf[];  // [4 or 2][RB*16][W]
 
   if ((int)blockIdx.x < p.n_app) {
-    // fused decode step: write the new K/V and low-rank rows; the items below
-    // read only keys cached before this step
+    // fused decode step: write the new low-rank rows and page-table entries;
+    // the items below read only keys cached before this step
     append_block(p.app, blockIdx.x, reinterpret_cast<char*>(s_buf));
     return;
   }
@@ -479,9 +480,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
   const int j = item % p.items_per_head;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = lane & 15, q = lane >> 4;
-  const int total = p.seg_off[p.n];
-  const int f0 = j * p.split;
-  const int n_ck = (min(f0 + p.split, total) - f0) / 32;
+  const int c_lo = (int)((int64_t)j * p.head_chunks / p.items_per_head);
+  const int c_hi = (int)((int64_t)(j + 1) * p.head_chunks / p.items_per_head);
+  const int f0 = 32 * c_lo;
+  const int n_ck = c_hi - c_lo;
 
   // chunk descriptors: segment (0 = shared, 1 + a = agent a's suffix), first key, page
   for (int c = threadIdx.x; c < n_ck; c += blockDim.x) {
@@ -637,83 +639,71 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     }
   }
 
-  // Combine the four waves: with one row block every wave parks its state in
-  // LDS; with more, waves 2 and 3 park theirs and waves 0 and 1 fold them in.
-  // Then every thread merges the parked states and writes the item's partial
-  // rows (o, o_lr, m, l) for the merge pass.
-  const int W = p.W;
-  const int RP = RB * 16;
+  // Fold the four waves' states pairwise through LDS (waves 2 and 3 into 0 and
+  // 1, then 1 into 0), each lane exchanging exactly the accumulator quads it
+  // holds, so the slots are read and written conflict-free in MFMA layout.
+  // Wave 0 then writes the item's partial rows (o, o_lr, m, l) for the merge.
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) l_run[rb] = xsum16_32(l_run[rb]);
-  auto park = [&](float* buf, bool fold) {
+  constexpr int NQ = DB + MB;  // accumulator quads per lane and row block
+  f32x4* const s_st = reinterpret_cast<f32x4*>(s_buf);                  // [2][RB][NQ][64]
+  float* const s_ml = reinterpret_cast<float*>(s_st + 2 * RB * NQ * 64);  // [2][RB][2][64]
+  auto put = [&](int slot) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const int rho = rb * 16 + n;
-      float* row = buf + rho * W;
-      const int a = min(rho / p.G, p.n - 1);
-      const int pidx = p.ag_pidx[a];
-      float a_old = 0.f, a_new = 1.f, m_c = m_run[rb];
-      if (fold) {
-        const float m_old = row[D + p.r];
-        m_c = fmaxf(m_old, m_run[rb]);
-        a_old = __builtin_amdgcn_exp2f(m_old - m_c);
-        a_new = __builtin_amdgcn_exp2f(m_run[rb] - m_c);
-      }
+      f32x4* const st = s_st + (slot * RB + rb) * NQ * 64 + lane;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db) st[db * 64] = oacc[rb][db];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          float* dst = row + db * 16 + 4 * q + jj;
-          *dst = (fold ? a_old * *dst : 0.f) + a_new * oacc[rb][db][jj];
-        }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int sr = mb * 16 + 4 * q + jj;
-          if (sr / p.r == pidx) {
-            float* dst = row + D + sr % p.r;
-            *dst = (fold ? a_old * *dst : 0.f) + a_new * lacc[rb][mb][jj];
-          }
-        }
-      if (q == 0) {
-        const float l_old = fold ? row[D + p.r + 1] : 0.f;
-        row[D + p.r + 1] = a_old * l_old + a_new * l_run[rb];
-        row[D + p.r] = m_c;
-      }
+      for (int mb = 0; mb < MB; ++mb) st[(DB + mb) * 64] = lacc[rb][mb];
+      s_ml[((slot * RB + rb) * 2) * 64 + lane] = m_run[rb];
+      s_ml[((slot * RB + rb) * 2 + 1) * 64 + lane] = l_run[rb];
     }
   };
-  constexpr int NB = RB == 1 ? 4 : 2;  // wave states left in LDS for the final merge
-  if (NB == 4) {
-    park(s_buf + w * RP * W, false);
-    __syncthreads();
-  } else {
-    if (w >= 2) park(s_buf + (w - 2) * RP * W, false);
-    __syncthreads();
-    if (w < 2) park(s_buf + w * RP * W, true);
-    __syncthreads();
-  }
-  float* dst = p.part + (uint64_t)item * p.R * W;
-  const int E = D + p.r;
-  for (int i = threadIdx.x; i < p.R * E; i += blockDim.x) {
-    const int rho = i / E, e = i % E;
-    float mb[NB], mc = -1e30f;
+  auto fold = [&](int slot) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      mb[b] = s_buf[(b * RP + rho) * W + E];
-      mc = fmaxf(mc, mb[b]);
-    }
-    float acc = 0.f, lsum = 0.f;
+    for (int rb = 0; rb < RB; ++rb) {
+      const f32x4* const st = s_st + (slot * RB + rb) * NQ * 64 + lane;
+      const float mo = s_ml[((slot * RB + rb) * 2) * 64 + lane];
+      const float lo = s_ml[((slot * RB + rb) * 2 + 1) * 64 + lane];
+      const float mc = fmaxf(m_run[rb], mo);
+      const float a = __builtin_amdgcn_exp2f(m_run[rb] - mc), b = __builtin_amdgcn_exp2f(mo - mc);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const float wt = __builtin_amdgcn_exp2f(mb[b] - mc);
-      acc += wt * s_buf[(b * RP + rho) * W + e];
-      lsum += wt * s_buf[(b * RP + rho) * W + E + 1];
+      for (int db = 0; db < DB; ++db) oacc[rb][db] = oacc[rb][db] * a + st[db * 64] * b;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) lacc[rb][mb] = lacc[rb][mb] * a + st[(DB + mb) * 64] * b;
+      l_run[rb] = l_run[rb] * a + lo * b;
+      m_run[rb] = mc;
     }
-    dst[rho * W + e] = acc;
-    if (e == 0) {
-      dst[rho * W + E] = mc;
-      dst[rho * W + E + 1] = lsum;
+  };
+  if (w >= 2) put(w - 2);
+  __syncthreads();
+  if (w < 2) fold(w);
+  if (w == 1) put(1);
+  __syncthreads();
+  if (w != 0) return;
+  fold(1);
+  const int W = p.W;
+  float* const dst = p.part + (uint64_t)item * p.R * W;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int rho = rb * 16 + n;
+    if (rho >= p.R) continue;
+    float* const row = dst + rho * W;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(row + db * 16 + 4 * q) = oacc[rb][db];
+    // keep the stacked low-rank entries of the row's own plane
+    const int pidx = p.ag_pidx[rho / p.G];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int sr = mb * 16 + 4 * q + jj;
+        if (sr / p.r == pidx) row[D + sr % p.r] = lacc[rb][mb][jj];
+      }
+    if (q == 0) {
+      row[D + p.r] = m_run[rb];
+      row[D + p.r + 1] = l_run[rb];
     }
   }
 }
@@ -739,6 +729,9 @@ struct MergeParams {
   uint64_t lr_plane;
   int new_page[SKV_MAX_AGENTS], new_slot[SKV_MAX_AGENTS], plane[SKV_MAX_AGENTS];
   float scale_log2;
+  int n_rows;       // leading blocks merge rows; the n_app after them copy the new K/V rows
+  int n_app;
+  AppendParams app;
 };
 
 // One workgroup per query row (agent, query head). Merges the row's partial
@@ -751,6 +744,13 @@ struct MergeParams {
 constexpr int kMergeVec = 8;  // slots per thread held in registers
 
 __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
+  extern __shared__ __attribute__((aligned(16))) char s_app[];  // append blocks' staging
+  if ((int)blockIdx.x >= p.n_rows) {
+    // fused decode step: copy the new K/V rows into the pages; the rows merged
+    // here take the new token from the step's inputs instead
+    append_block(p.app, blockIdx.x - p.n_rows, s_app);
+    return;
+  }
   __shared__ float s_w[kMaxMergeSlots];
   __shared__ f32x4 s_red[8][40];
   __shared__ float s_v[128 + 32];
@@ -1121,7 +1121,8 @@ int w_of(const skv::Geometry& g) { return g.D + g.r + 4; }
 
 template <int D, int RB, int MB>
 int launch_split_t(const skv::Geometry& g, const DecodeParams& p, int items) {
-  size_t lds = (size_t)(RB == 1 ? 4 : 2) * RB * 16 * p.W * sizeof(float);
+  constexpr int DB = D / 16, NQ = DB + MB;
+  size_t lds = (size_t)2 * RB * (NQ * 64 * 16 + 2 * 64 * 4);          // two slots of wave states
   if (p.n_app > 0) lds = std::max(lds, (size_t)64 * (128 + 8) * 2);  // append blocks' staging
   return launch(g, 2, decode_split_kernel<D, RB, MB>, dim3(p.n_app + items), lds, p,
                 "decode_split_kernel");
@@ -1234,36 +1235,15 @@ static int decode_impl(const Geometry& g, const AttnJob& job, const AppendJob* a
       p.ag_pidx[i] = pidx;
       max_b = std::max(max_b, a.b);
     }
-    // flattened key sequence per KV head: shared prefix, then each own suffix,
-    // each padded to whole 32-key chunks
-    p.shared_len = (max_b + 31) / 32 * 32;
-    p.seg_off[0] = p.shared_len;
-    for (int i = 0; i < n; ++i) p.seg_off[i + 1] = p.seg_off[i] + (p.ag_S[i] + 31) / 32 * 32;
-    const int total = p.seg_off[n];
-    // items: about one per CU over all KV heads, in whole 32-key chunks
-    const int chunks = total / 32;
-    int per_head = std::max(1, std::min(chunks, kCUs / g.Hkv));
-    int split = std::max(32, (chunks + per_head - 1) / per_head * 32);
-    if (split > kMaxItemChunks * 32) split = kMaxItemChunks * 32;
-    const int items_per_head = (total + split - 1) / split;  // 0 when nothing is cached yet
-    if ((uint64_t)items_per_head * g.Hkv > (uint64_t)kMaxItems || items_per_head > kMaxMergeSlots) {
-      snprintf(g_err, sizeof g_err, "decode view too long for the split plan (%d keys)", total);
-      return SKV_ERR_UNSUPPORTED;
-    }
-    p.split = split;
-    p.items_per_head = items_per_head;
-    p.scale_log2 = 1.4426950408889634f / sqrtf((float)g.D);
-    int rb = (p.R + 15) / 16;
-    rb = rb <= 1 ? 1 : (rb <= 2 ? 2 : 4);
-    int mb = (p.n_planes * g.r + 15) / 16;
-    mb = mb <= 1 ? 1 : (mb <= 2 ? 2 : (mb <= 4 ? 4 : 8));
-    const int items = items_per_head * g.Hkv;
+    // A fused step writes the group's new rows: the low-rank rows (and new
+    // page-table entries) from leading blocks of the split launch, which the
+    // merge reads back for the new token; the K/V rows from trailing blocks of
+    // the merge launch, which takes them from the inputs.
+    AppendJob sub{};
+    AppendParams kv_app{};
+    int n_kv_app = 0;
     if (app) {
-      AppendJob sub{};
       sub.layer = app->layer;
-      sub.do_kv = app->do_kv;
-      sub.do_lr = app->do_lr;
-      sub.update_tables = app->update_tables;
       sub.k = app->k;
       sub.v = app->v;
       sub.x = app->x;
@@ -1274,11 +1254,47 @@ static int decode_impl(const Geometry& g, const AttnJob& job, const AppendJob* a
         sub.n_ids += sp.n_pages;
         sub.spans[sub.n_spans++] = sp;
       }
+      sub.do_kv = false;
+      sub.do_lr = app->do_lr;
+      sub.update_tables = app->update_tables;
       plan_append(g, sub, p.app);
       p.n_app = append_blocks(p.app);
-      if (p.n_app == 0) p.n_app = 1;  // the table update rides on block 0
+      if (p.n_app == 0 && sub.update_tables) p.n_app = 1;  // the table update rides on block 0
+      sub.do_kv = app->do_kv;
+      sub.do_lr = false;
+      sub.update_tables = false;
+      plan_append(g, sub, kv_app);
+      n_kv_app = append_blocks(kv_app);
     }
-    int rc = g.D == 128 ? launch_split_d<128>(g, rb, mb, p, items) : launch_split_d<64>(g, rb, mb, p, items);
+    // flattened key sequence per KV head: shared prefix, then each own suffix,
+    // each padded to whole 32-key chunks
+    p.shared_len = (max_b + 31) / 32 * 32;
+    p.seg_off[0] = p.shared_len;
+    for (int i = 0; i < n; ++i) p.seg_off[i + 1] = p.seg_off[i] + (p.ag_S[i] + 31) / 32 * 32;
+    const int chunks = p.seg_off[n] / 32;
+    // items: as many per KV head as leave one CU per workgroup next to the
+    // append blocks, each a balanced run of whole chunks (0 items when nothing
+    // is cached yet)
+    int items_per_head = 0;
+    if (chunks > 0) {
+      items_per_head = std::min(chunks, std::max(1, (kCUs - p.n_app) / g.Hkv));
+      items_per_head = std::max(items_per_head, (chunks + kMaxItemChunks - 1) / kMaxItemChunks);
+    }
+    if ((uint64_t)items_per_head * g.Hkv > (uint64_t)kMaxItems || items_per_head > kMaxMergeSlots) {
+      snprintf(g_err, sizeof g_err, "decode view too long for the split plan (%d keys)", p.seg_off[n]);
+      return SKV_ERR_UNSUPPORTED;
+    }
+    p.head_chunks = chunks;
+    p.items_per_head = items_per_head;
+    p.scale_log2 = 1.4426950408889634f / sqrtf((float)g.D);
+    int rb = (p.R + 15) / 16;
+    rb = rb <= 1 ? 1 : (rb <= 2 ? 2 : 4);
+    int mb = (p.n_planes * g.r + 15) / 16;
+    mb = mb <= 1 ? 1 : (mb <= 2 ? 2 : (mb <= 4 ? 4 : 8));
+    const int items = items_per_head * g.Hkv;
+    int rc = SKV_OK;
+    if (p.n_app + items > 0)
+      rc = g.D == 128 ? launch_split_d<128>(g, rb, mb, p, items) : launch_split_d<64>(g, rb, mb, p, items);
     if (rc != SKV_OK) return rc;
     MergeParams mp{};
     mp.part = part;
@@ -1308,8 +1324,12 @@ static int decode_impl(const Geometry& g, const AttnJob& job, const AppendJob* a
         mp.plane[i] = sp.plane;
       }
       mp.scale_log2 = p.scale_log2;
+      mp.app = kv_app;
+      mp.n_app = n_kv_app;
     }
-    rc = launch(g, 3, decode_merge_kernel, dim3(n * g.Hkv * g.G), 0, mp, "decode_merge_kernel");
+    mp.n_rows = n * g.Hkv * g.G;
+    rc = launch(g, 3, decode_merge_kernel, dim3(mp.n_rows + mp.n_app),
+                mp.n_app ? (size_t)64 * (128 + 8) * 2 : 0, mp, "decode_merge_kernel");
     if (rc != SKV_OK) return rc;
   }
   return SKV_OK;
