@@ -598,21 +598,30 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
       for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
       mx = xmax16_32(mx);
       const float m_new = fmaxf(m_run[rb], mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
       float pv[8], ps = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         pv[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
         ps += pv[i];
       }
-      l_run[rb] = l_run[rb] * alpha + ps;
-      m_run[rb] = m_new;
+      // rescale the accumulators only when some row's running max grew
+      // (rare once the maxima settle); otherwise the scale factor is 1
+      if (__any(m_new > m_run[rb])) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[rb][db] *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) lacc[rb][mb] *= alpha;
+        m_run[rb] = m_new;
+      }
+      l_run[rb] += ps;
       const bf16x8 pt = pack8(pv);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[rb][db] = mfma(ch.v[db], pt, oacc[rb][db] * alpha);
+      for (int db = 0; db < DB; ++db) oacc[rb][db] = mfma(ch.v[db], pt, oacc[rb][db]);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-        lacc[rb][mb] = mfma(__builtin_bit_cast(bf16x8, ch.l[mb] & lr_mask[mb]), pt, lacc[rb][mb] * alpha);
+        lacc[rb][mb] = mfma(__builtin_bit_cast(bf16x8, ch.l[mb] & lr_mask[mb]), pt, lacc[rb][mb]);
     }
   };
   const int n_chunks = w < n_ck ? (n_ck - w + 3) / 4 : 0;  // this wave's chunks: w, w + 4, ...
@@ -861,9 +870,6 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
 // Prefill
 // ---------------------------------------------------------------------------
 
-constexpr int kPrefRBW = 2;                    // 16-row blocks per wave
-constexpr int kPrefRows = 4 * 16 * kPrefRBW;   // query rows per workgroup
-
 struct PrefillParams {
   const u16* K;
   const u16* VT;
@@ -882,9 +888,33 @@ struct PrefillParams {
   float scale_log2;
 };
 
-template <int D, int MB>
+// LDS image of one page of one KV head: the K tile and the V^T tile (64 x D
+// each, in operand order) and the page's low-rank rows (r x 64).
+template <int D>
+constexpr int prefill_page_elems() { return 2 * 64 * D + 32 * 64; }
+
+// Copy one 1 KB operand block from global memory into LDS: every lane moves
+// 16 bytes, lane l landing at dst + 16 l (the DMA places a wave's data
+// contiguously from the LDS base it is given).
+__device__ __forceinline__ void dma_block(const u16* src_wave, u16* dst_wave, int lane) {
+  __builtin_amdgcn_global_load_lds((const void*)(src_wave + lane * 8),
+                                   (void __attribute__((address_space(3)))*)dst_wave, 16, 0, 0);
+}
+
+// Suffix prefill: a workgroup takes 64 RB query rows (rows = query position x
+// query head of one KV head) and streams the view's pages once: each page's K,
+// V^T and low-rank rows are copied to LDS by the whole workgroup through a ring
+// of three buffers (the copies of the next two pages run during this page's
+// compute), and every wave reads the MFMA operands of its 16 RB rows from LDS,
+// so one K/V tile read serves RB row blocks. Scores stay in registers as in
+// decode (S^T = K Q^T with permuted K rows); causal and segment masks are
+// applied per key, except on 32-key halves every row of the wave sees whole.
+template <int D, int MB, int RB>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
-  constexpr int KS = D / 32, DB = D / 16, RB = kPrefRBW;
+  constexpr int KS = D / 32, DB = D / 16;
+  constexpr int ROWS = 4 * 16 * RB;
+  constexpr int PE = prefill_page_elems<D>();
+  extern __shared__ __attribute__((aligned(16))) u16 s_kv[];  // [3][PE]
   __shared__ int32_t s_pages[kMaxViewPages];
   __shared__ float s_lr[4][16][33];
   const int g = blockIdx.x % p.Hkv;
@@ -894,21 +924,22 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
   qb -= p.blk0[ai];
   const int b = p.ag_b[ai], S = p.ag_S[ai], nq = p.ag_nq[ai];
   const int Lv = b + S;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, q = lane >> 4;
   const int rows_total = nq * p.G;
-  const int row_blk0 = qb * kPrefRows;
+  const int row_blk0 = qb * ROWS;
   // highest view position among this block's rows
-  const int last_row = min(row_blk0 + kPrefRows, rows_total) - 1;
+  const int last_row = min(row_blk0 + ROWS, rows_total) - 1;
   const int t_max = Lv - nq + last_row / p.G;
 
   const int np_sh = (min(b, t_max + 1) + kPage - 1) / kPage;
   const int own_keys = max(0, min(S, t_max + 1 - b));
   const int np_own = (own_keys + kPage - 1) / kPage;
+  const int n_pages = np_sh + np_own;
   const int32_t* tsh = p.tbl;
   const int32_t* tow = p.tbl + (1 + p.ag_id[ai]) * p.tbl_seq;
-  for (int i = threadIdx.x; i < np_sh + np_own; i += blockDim.x)
-    s_pages[i] = i < np_sh ? tsh[i] : tow[i - np_sh];
+  for (int i = threadIdx.x; i < n_pages; i += blockDim.x) s_pages[i] = i < np_sh ? tsh[i] : tow[i - np_sh];
 
   bf16x8 qf[RB][KS];
   int tpos[RB];
@@ -922,11 +953,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[rb][s] = ok ? ld8(qp + 32 * s + 8 * q) : zero8();
   }
-  const int plane = p.ag_plane[ai];
-  const u16* lrb = p.LRT + (uint64_t)plane * p.lr_plane;
-  bool lr_ok[MB];
+  const u16* lrb = p.LRT + (uint64_t)p.ag_plane[ai] * p.lr_plane;
+  const int lr_blocks = (p.r * 64 * 2 + 1023) / 1024;  // 1 KB blocks of a page's low-rank rows
+  // lowest view position among the wave's valid rows: a key at or below it is
+  // visible to all of them
+  int tmin = 0x7fffffff;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) lr_ok[mb] = mb * 16 + n < p.r;
+  for (int rb = 0; rb < RB; ++rb)
+    if (tpos[rb] >= 0) tmin = min(tmin, tpos[rb]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) tmin = min(tmin, __shfl_xor(tmin, o));
+  tmin = __builtin_amdgcn_readfirstlane(tmin);
+  uint32_t lr_mask[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) lr_mask[mb] = mb * 16 + n < p.r ? 0xffffffffu : 0u;
 
   float m_run[RB], l_run[RB];
   f32x4 oacc[RB][DB], lacc[RB][MB];
@@ -939,34 +979,76 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) lacc[rb][mb] = f32x4{0, 0, 0, 0};
   }
-  __syncthreads();
+  __syncthreads();  // s_pages
 
   const uint64_t head_off = (uint64_t)g * kPage * D;
   const uint64_t page_elems = (uint64_t)p.Hkv * kPage * D;
-  // Two segments: shared view positions [0, b) and own positions [0, S) at b + j.
-  for (int seg = 0; seg < 2; ++seg) {
-    const int nkeys = seg == 0 ? min(b, t_max + 1) : own_keys;
-    const int vbase = seg == 0 ? 0 : b;         // view position of segment key 0
-    const int seg_lim = seg == 0 ? b : S;       // keys beyond the segment are invalid
-    const int pg_off = seg == 0 ? 0 : np_sh;
-    for (int c = 0; c * 32 < nkeys; ++c) {
-      const int key0 = c * 32;
-      const int page = s_pages[pg_off + key0 / kPage];
-      const int half = (key0 % kPage) / 32;
-      const u16* kp = p.K + (uint64_t)page * page_elems + head_off + half * (2 * KS * 512) + lane * 8;
+  // The workgroup's copy of page i into LDS buffer buf: each wave moves D / 32
+  // of the K tile's 1 KB blocks, as many of the V^T tile's, and one 1 KB block
+  // of low-rank rows (waves past the page's block count repeat block 0, the
+  // same bytes to the same place), so every wave issues the same number of
+  // copies (kCopies) and the wait below can count them. With r = 4 the block
+  // runs 512 bytes past the page's rows, inside the arena; those rows are never
+  // read.
+  auto copy_page = [&](int i, int buf) {
+    const int page = s_pages[i];
+    const u16* kp = p.K + (uint64_t)page * page_elems + head_off;
+    const u16* vp = p.VT + (uint64_t)page * page_elems + head_off;
+    u16* dst = s_kv + buf * PE;
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u) {
+      const int blk = w * (D / 32) + u;
+      dma_block(kp + blk * 512, dst + blk * 512, lane);
+      dma_block(vp + blk * 512, dst + 64 * D + blk * 512, lane);
+    }
+    const int lb = w < lr_blocks ? w : 0;
+    dma_block(lrb + (uint64_t)page * p.r * kPage + lb * 512, dst + 2 * 64 * D + lb * 512, lane);
+  };
+  constexpr int kCopies = 2 * (D / 32) + 1;  // copies one wave issues per page
+  // s_waitcnt with only vmcnt limited (expcnt and lgkmcnt at their maxima)
+  constexpr int kWaitOnePage = (kCopies & 15) | ((kCopies >> 4) << 14) | (7 << 4) | (15 << 8);
+
+  // Ring of three page buffers: page i is computed from buffer i % 3 while the
+  // copies of pages i + 1 and i + 2 are in flight. Before the barrier that
+  // publishes page i + 1, each wave waits until only its copies of page i + 2
+  // are outstanding; buffer (i + 2) % 3 was last read in iteration i - 1,
+  // before the previous barrier. The page list is clamped at the end, so every
+  // iteration issues one page of copies (the surplus ones are never read).
+  auto clampi = [&](int i) { return min(i, n_pages - 1); };
+  if (n_pages > 0) {
+    copy_page(0, 0);
+    copy_page(clampi(1), 1);
+    __builtin_amdgcn_s_waitcnt(kWaitOnePage);
+    __builtin_amdgcn_s_barrier();
+  }
+  for (int i = 0; i < n_pages; ++i) {
+    const int buf = i % 3;
+    copy_page(clampi(i + 2), (i + 2) % 3);
+    const bool own = i >= np_sh;
+    const int pg_key0 = (own ? i - np_sh : i) * kPage;  // first key of the page in its segment
+    const int vbase = own ? b : 0;                       // view position of segment key 0
+    const int seg_lim = own ? S : b;                     // keys beyond the segment are invalid
+    const u16* kv = s_kv + buf * PE;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int key0 = pg_key0 + h * 32;
+      // every row of the wave sees all 32 keys of this half
+      const bool whole = key0 + 32 <= seg_lim && vbase + key0 + 31 <= tmin;
       bf16x8 kf[2][KS], vf[DB], lf[MB];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int s = 0; s < KS; ++s) kf[t][s] = ld8(kp + (t * KS + s) * 512);
-      const u16* vp = p.VT + (uint64_t)page * page_elems + head_off + half * (DB * 512) + lane * 8;
+        for (int s = 0; s < KS; ++s)
+          kf[t][s] = *reinterpret_cast<const bf16x8*>(kv + ((h * 2 + t) * KS + s) * 512 + lane * 8);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) vf[db] = ld8(vp + db * 512);
+      for (int db = 0; db < DB; ++db)
+        vf[db] = *reinterpret_cast<const bf16x8*>(kv + 64 * D + (h * DB + db) * 512 + lane * 8);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        lf[mb] = lr_ok[mb] ? ld8(lrb + (uint64_t)page * p.r * kPage + (mb * 16 + n) * kPage +
-                                 half * 32 + 8 * q)
-                           : zero8();
+      for (int mb = 0; mb < MB; ++mb) {
+        const int k = min(mb * 16 + n, p.r - 1);
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(kv + 2 * 64 * D + k * kPage + h * 32 + 8 * q);
+        lf[mb] = __builtin_bit_cast(bf16x8, raw & lr_mask[mb]);
+      }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         f32x4 s0 = {0, 0, 0, 0}, s1 = {0, 0, 0, 0};
@@ -976,36 +1058,57 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
           s1 = mfma(kf[1][s], qf[rb][s], s1);
         }
         float sc[8];
+        if (whole) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int kA = key0 + 8 * q + jj, kB = kA + 4;
-          const bool okA = kA < seg_lim && vbase + kA <= tpos[rb];
-          const bool okB = kB < seg_lim && vbase + kB <= tpos[rb];
-          sc[jj] = okA ? s0[jj] * p.scale_log2 : -INFINITY;
-          sc[jj + 4] = okB ? s1[jj] * p.scale_log2 : -INFINITY;
+          for (int jj = 0; jj < 4; ++jj) {
+            sc[jj] = s0[jj] * p.scale_log2;
+            sc[jj + 4] = s1[jj] * p.scale_log2;
+          }
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int kA = key0 + 8 * q + jj, kB = kA + 4;
+            const bool okA = kA < seg_lim && vbase + kA <= tpos[rb];
+            const bool okB = kB < seg_lim && vbase + kB <= tpos[rb];
+            sc[jj] = okA ? s0[jj] * p.scale_log2 : -INFINITY;
+            sc[jj + 4] = okB ? s1[jj] * p.scale_log2 : -INFINITY;
+          }
         }
         float mx = sc[0];
 #pragma unroll
-        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
+        for (int j2 = 1; j2 < 8; ++j2) mx = fmaxf(mx, sc[j2]);
         mx = xmax16_32(mx);
         const float m_new = fmaxf(m_run[rb], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
         float pv[8], ps = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          pv[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
-          ps += pv[i];
+        for (int j2 = 0; j2 < 8; ++j2) {
+          pv[j2] = __builtin_amdgcn_exp2f(sc[j2] - m_new);
+          ps += pv[j2];
         }
-        l_run[rb] = l_run[rb] * alpha + ps;
-        m_run[rb] = m_new;
+        // rescale the accumulators only when some row's running max grew
+        // (rare once the maxima settle); otherwise the scale factor is 1
+        if (__any(m_new > m_run[rb])) {
+          const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+          l_run[rb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[rb][db] *= alpha;
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) lacc[rb][mb] *= alpha;
+          m_run[rb] = m_new;
+        }
+        l_run[rb] += ps;
         const bf16x8 pt = pack8(pv);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[rb][db] = mfma(vf[db], pt, oacc[rb][db] * alpha);
+        for (int db = 0; db < DB; ++db) oacc[rb][db] = mfma(vf[db], pt, oacc[rb][db]);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) lacc[rb][mb] = mfma(lf[mb], pt, lacc[rb][mb] * alpha);
+        for (int mb = 0; mb < MB; ++mb) lacc[rb][mb] = mfma(lf[mb], pt, lacc[rb][mb]);
       }
     }
+    __builtin_amdgcn_s_waitcnt(kWaitOnePage);  // this wave's copies of page i + 1 have landed
+    __builtin_amdgcn_s_barrier();              // ... and every other wave's; buffer i % 3 is free
   }
+  __builtin_amdgcn_s_waitcnt(0);  // surplus copies of the last iterations
+  __syncthreads();
 
   // finalize: o = (oacc + lacc . B_i) / l, B_i applied once for the block's rows
   const int HD = p.Hkv * D;
@@ -1126,6 +1229,27 @@ int launch_split_t(const skv::Geometry& g, const DecodeParams& p, int items) {
   if (p.n_app > 0) lds = std::max(lds, (size_t)64 * (128 + 8) * 2);  // append blocks' staging
   return launch(g, 2, decode_split_kernel<D, RB, MB>, dim3(p.n_app + items), lds, p,
                 "decode_split_kernel");
+}
+
+// 16-row blocks per wave in prefill: four, or two with rank 32 (two low-rank
+// blocks), where four would not fit the registers
+constexpr int prefill_rb(int mb) { return mb == 1 ? 4 : 2; }
+constexpr int prefill_rows(int mb) { return 4 * 16 * prefill_rb(mb); }  // query rows per workgroup
+
+template <int D, int MB>
+int launch_prefill(const skv::Geometry& g, const PrefillParams& p, int blocks) {
+  constexpr int kPrefRB = prefill_rb(MB);
+  const size_t lds = (size_t)3 * prefill_page_elems<D>() * sizeof(u16);
+  // the page ring exceeds the default dynamic LDS limit (set once per process;
+  // the attribute holds for every device)
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(prefill_kernel<D, MB, kPrefRB>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) {
+    set_err("hipFuncSetAttribute(prefill_kernel)", attr);
+    return SKV_ERR_HIP;
+  }
+  return launch(g, 4, prefill_kernel<D, MB, kPrefRB>, dim3(blocks), lds, p, "prefill_kernel");
 }
 
 template <int D>
@@ -1364,6 +1488,8 @@ int dev_attn_prefill(const Geometry& g, const AttnJob& job) {
   p.r = g.r;
   p.n = job.n;
   p.blk0[0] = 0;
+  const int mb = (g.r + 15) / 16;
+  const int rows = prefill_rows(mb);
   for (int i = 0; i < job.n; ++i) {
     const AttnAgent& a = job.ag[i];
     if ((a.b + kPage - 1) / kPage + (a.S + kPage - 1) / kPage > kMaxViewPages) {
@@ -1376,16 +1502,14 @@ int dev_attn_prefill(const Geometry& g, const AttnJob& job) {
     p.ag_plane[i] = a.plane;
     p.ag_nq[i] = a.n_q;
     p.ag_row0[i] = a.q_row0;
-    p.blk0[i + 1] = p.blk0[i] + (a.n_q * g.G + kPrefRows - 1) / kPrefRows;
+    p.blk0[i + 1] = p.blk0[i] + (a.n_q * g.G + rows - 1) / rows;
   }
   p.scale_log2 = 1.4426950408889634f / sqrtf((float)g.D);
   const int blocks = p.blk0[job.n] * g.Hkv;
-  const int mb = (g.r + 15) / 16;
+  if (blocks == 0) return SKV_OK;
   if (g.D == 128)
-    return mb == 1 ? launch(g, 4, prefill_kernel<128, 1>, dim3(blocks), 0, p, "prefill_kernel")
-                   : launch(g, 4, prefill_kernel<128, 2>, dim3(blocks), 0, p, "prefill_kernel");
-  return mb == 1 ? launch(g, 4, prefill_kernel<64, 1>, dim3(blocks), 0, p, "prefill_kernel")
-                 : launch(g, 4, prefill_kernel<64, 2>, dim3(blocks), 0, p, "prefill_kernel");
+    return mb == 1 ? launch_prefill<128, 1>(g, p, blocks) : launch_prefill<128, 2>(g, p, blocks);
+  return mb == 1 ? launch_prefill<64, 1>(g, p, blocks) : launch_prefill<64, 2>(g, p, blocks);
 }
 
 int dev_sync(const Geometry& g) {
