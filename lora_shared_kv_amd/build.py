@@ -21,9 +21,12 @@ OUT = os.path.join(PKG, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-# Packed fp32 ops are turned off for every HIP translation unit.
+# Packed fp32 ops are turned off for every HIP translation unit. MFMA
+# accumulators are kept in VGPRs (the VGPR form of the MFMA instructions): the
+# kernels rescale them with vector ops, which cannot read AGPRs.
 HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC,
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-mfma-vgpr-form",
              "-Wno-unused-result"]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I" + INCLUDE, "-I" + CSRC]
 

@@ -901,22 +901,24 @@ __device__ __forceinline__ void dma_block(const u16* src_wave, u16* dst_wave, in
                                    (void __attribute__((address_space(3)))*)dst_wave, 16, 0, 0);
 }
 
-// Suffix prefill: a workgroup takes 64 RB query rows (rows = query position x
-// query head of one KV head) and streams the view's pages once: each page's K,
+// Suffix prefill: a workgroup of NW waves takes 16 NW RB query rows (rows =
+// query position x query head of one KV head) and streams the view's pages once: each page's K,
 // V^T and low-rank rows are copied to LDS by the whole workgroup through a ring
 // of three buffers (the copies of the next two pages run during this page's
 // compute), and every wave reads the MFMA operands of its 16 RB rows from LDS,
 // so one K/V tile read serves RB row blocks. Scores stay in registers as in
 // decode (S^T = K Q^T with permuted K rows); causal and segment masks are
 // applied per key, except on 32-key halves every row of the wave sees whole.
-template <int D, int MB, int RB>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
+template <int D, int MB, int RB, int NW>
+__global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
   constexpr int KS = D / 32, DB = D / 16;
-  constexpr int ROWS = 4 * 16 * RB;
+  constexpr int ROWS = NW * 16 * RB;
   constexpr int PE = prefill_page_elems<D>();
+  constexpr int KB = D / 8 / NW;  // 1 KB blocks of a K (or V^T) page tile each wave copies
+  static_assert(KB * NW * 8 == D, "page tile blocks must split evenly over the waves");
   extern __shared__ __attribute__((aligned(16))) u16 s_kv[];  // [3][PE]
   __shared__ int32_t s_pages[kMaxViewPages];
-  __shared__ float s_lr[4][16][33];
+  __shared__ float s_lr[NW][16][33];
   const int g = blockIdx.x % p.Hkv;
   int qb = blockIdx.x / p.Hkv;
   int ai = 0;
@@ -983,8 +985,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
 
   const uint64_t head_off = (uint64_t)g * kPage * D;
   const uint64_t page_elems = (uint64_t)p.Hkv * kPage * D;
-  // The workgroup's copy of page i into LDS buffer buf: each wave moves D / 32
-  // of the K tile's 1 KB blocks, as many of the V^T tile's, and one 1 KB block
+  // The workgroup's copy of page i into LDS buffer buf: each wave moves KB of
+  // the K tile's 1 KB blocks, as many of the V^T tile's, and one 1 KB block
   // of low-rank rows (waves past the page's block count repeat block 0, the
   // same bytes to the same place), so every wave issues the same number of
   // copies (kCopies) and the wait below can count them. With r = 4 the block
@@ -996,15 +998,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     const u16* vp = p.VT + (uint64_t)page * page_elems + head_off;
     u16* dst = s_kv + buf * PE;
 #pragma unroll
-    for (int u = 0; u < D / 32; ++u) {
-      const int blk = w * (D / 32) + u;
+    for (int u = 0; u < KB; ++u) {
+      const int blk = w * KB + u;
       dma_block(kp + blk * 512, dst + blk * 512, lane);
       dma_block(vp + blk * 512, dst + 64 * D + blk * 512, lane);
     }
     const int lb = w < lr_blocks ? w : 0;
     dma_block(lrb + (uint64_t)page * p.r * kPage + lb * 512, dst + 2 * 64 * D + lb * 512, lane);
   };
-  constexpr int kCopies = 2 * (D / 32) + 1;  // copies one wave issues per page
+  constexpr int kCopies = 2 * KB + 1;  // copies one wave issues per page
   // s_waitcnt with only vmcnt limited (expcnt and lgkmcnt at their maxima)
   constexpr int kWaitOnePage = (kCopies & 15) | ((kCopies >> 4) << 14) | (7 << 4) | (15 << 8);
 
@@ -1034,35 +1036,32 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
       const int key0 = pg_key0 + h * 32;
       // every row of the wave sees all 32 keys of this half
       const bool whole = key0 + 32 <= seg_lim && vbase + key0 + 31 <= tmin;
-      bf16x8 kf[2][KS], vf[DB], lf[MB];
+      // S^T = K Q^T for the RB row blocks, one 16-key score tile at a time
+      f32x4 sacc[RB][2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t) {
+        bf16x8 kf[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s)
-          kf[t][s] = *reinterpret_cast<const bf16x8*>(kv + ((h * 2 + t) * KS + s) * 512 + lane * 8);
+          kf[s] = *reinterpret_cast<const bf16x8*>(kv + ((h * 2 + t) * KS + s) * 512 + lane * 8);
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        vf[db] = *reinterpret_cast<const bf16x8*>(kv + 64 * D + (h * DB + db) * 512 + lane * 8);
+        for (int rb = 0; rb < RB; ++rb) {
+          f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int k = min(mb * 16 + n, p.r - 1);
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(kv + 2 * 64 * D + k * kPage + h * 32 + 8 * q);
-        lf[mb] = __builtin_bit_cast(bf16x8, raw & lr_mask[mb]);
+          for (int s = 0; s < KS; ++s) acc = mfma(kf[s], qf[rb][s], acc);
+          sacc[rb][t] = acc;
+        }
       }
+      // online softmax per row block; P^T stays in registers as the B operand
+      bf16x8 pt[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        f32x4 s0 = {0, 0, 0, 0}, s1 = {0, 0, 0, 0};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          s0 = mfma(kf[0][s], qf[rb][s], s0);
-          s1 = mfma(kf[1][s], qf[rb][s], s1);
-        }
         float sc[8];
         if (whole) {
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            sc[jj] = s0[jj] * p.scale_log2;
-            sc[jj + 4] = s1[jj] * p.scale_log2;
+            sc[jj] = sacc[rb][0][jj] * p.scale_log2;
+            sc[jj + 4] = sacc[rb][1][jj] * p.scale_log2;
           }
         } else {
 #pragma unroll
@@ -1070,8 +1069,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
             const int kA = key0 + 8 * q + jj, kB = kA + 4;
             const bool okA = kA < seg_lim && vbase + kA <= tpos[rb];
             const bool okB = kB < seg_lim && vbase + kB <= tpos[rb];
-            sc[jj] = okA ? s0[jj] * p.scale_log2 : -INFINITY;
-            sc[jj + 4] = okB ? s1[jj] * p.scale_log2 : -INFINITY;
+            sc[jj] = okA ? sacc[rb][0][jj] * p.scale_log2 : -INFINITY;
+            sc[jj + 4] = okB ? sacc[rb][1][jj] * p.scale_log2 : -INFINITY;
           }
         }
         float mx = sc[0];
@@ -1097,11 +1096,22 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
           m_run[rb] = m_new;
         }
         l_run[rb] += ps;
-        const bf16x8 pt = pack8(pv);
+        pt[rb] = pack8(pv);
+      }
+      // O^T += V^T P^T and L^T += LR^T P^T, one operand tile at a time
 #pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[rb][db] = mfma(vf[db], pt, oacc[rb][db]);
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(kv + 64 * D + (h * DB + db) * 512 + lane * 8);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) lacc[rb][mb] = mfma(lf[mb], pt, lacc[rb][mb]);
+        for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma(vf, pt[rb], oacc[rb][db]);
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int k = min(mb * 16 + n, p.r - 1);
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(kv + 2 * 64 * D + k * kPage + h * 32 + 8 * q);
+        const bf16x8 lf = __builtin_bit_cast(bf16x8, raw & lr_mask[mb]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) lacc[rb][mb] = mfma(lf, pt[rb], lacc[rb][mb]);
       }
     }
     __builtin_amdgcn_s_waitcnt(kWaitOnePage);  // this wave's copies of page i + 1 have landed
@@ -1183,7 +1193,7 @@ struct DevState {
 // measured interval is the kernel's own execution.
 template <typename Kernel, typename Params>
 int launch(const skv::Geometry& g, int kind, Kernel kernel, dim3 grid, size_t lds,
-           const Params& params, const char* what) {
+           const Params& params, const char* what, int threads = 256) {
   auto* st = (DevState*)g.dev;
   hipStream_t stream = (hipStream_t)g.stream;
   hipEvent_t a = nullptr, b = nullptr;
@@ -1192,10 +1202,10 @@ int launch(const skv::Geometry& g, int kind, Kernel kernel, dim3 grid, size_t ld
     b = st->get();
   }
   if (a && b) {
-    hipExtLaunchKernelGGL(kernel, grid, dim3(256), (uint32_t)lds, stream, a, b, 0, params);
+    hipExtLaunchKernelGGL(kernel, grid, dim3(threads), (uint32_t)lds, stream, a, b, 0, params);
     st->recs.push_back({kind, a, b});
   } else {
-    hipLaunchKernelGGL(kernel, grid, dim3(256), lds, stream, params);
+    hipLaunchKernelGGL(kernel, grid, dim3(threads), lds, stream, params);
   }
   ++*g.launches;
   hipError_t e = hipGetLastError();
@@ -1231,25 +1241,26 @@ int launch_split_t(const skv::Geometry& g, const DecodeParams& p, int items) {
                 "decode_split_kernel");
 }
 
-// 16-row blocks per wave in prefill: four, or two with rank 32 (two low-rank
-// blocks), where four would not fit the registers
-constexpr int prefill_rb(int mb) { return mb == 1 ? 4 : 2; }
-constexpr int prefill_rows(int mb) { return 4 * 16 * prefill_rb(mb); }  // query rows per workgroup
+// Prefill workgroups: eight waves of two 16-row blocks each (two waves per
+// SIMD, accumulators in VGPRs), 256 query rows per workgroup.
+constexpr int kPrefNW = 8;
+constexpr int kPrefRB = 2;
+constexpr int prefill_rows(int) { return kPrefNW * 16 * kPrefRB; }
 
 template <int D, int MB>
 int launch_prefill(const skv::Geometry& g, const PrefillParams& p, int blocks) {
-  constexpr int kPrefRB = prefill_rb(MB);
   const size_t lds = (size_t)3 * prefill_page_elems<D>() * sizeof(u16);
   // the page ring exceeds the default dynamic LDS limit (set once per process;
   // the attribute holds for every device)
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(prefill_kernel<D, MB, kPrefRB>),
+      reinterpret_cast<const void*>(prefill_kernel<D, MB, kPrefRB, kPrefNW>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) {
     set_err("hipFuncSetAttribute(prefill_kernel)", attr);
     return SKV_ERR_HIP;
   }
-  return launch(g, 4, prefill_kernel<D, MB, kPrefRB>, dim3(blocks), lds, p, "prefill_kernel");
+  return launch(g, 4, prefill_kernel<D, MB, kPrefRB, kPrefNW>, dim3(blocks), lds, p, "prefill_kernel",
+                64 * kPrefNW);
 }
 
 template <int D>
