@@ -84,14 +84,22 @@ __device__ __forceinline__ bf16x8 pack8(const float* p) {
   return r;
 }
 
-__device__ __forceinline__ float xmax16_32(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+// Reductions over the four lanes n, n + 16, n + 32, n + 48 (the lane groups
+// that hold one MFMA column): v_permlane16_swap / v_permlane32_swap with both
+// operands = v return, per lane, v at the lane and at the lane 16 (32) apart,
+// as plain VALU ops.
+__device__ __forceinline__ float xpair16(float v, float (*op)(float, float)) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float xsum16_32(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+__device__ __forceinline__ float xpair32(float v, float (*op)(float, float)) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+__device__ __forceinline__ float fmax_op(float a, float b) { return fmaxf(a, b); }
+__device__ __forceinline__ float add_op(float a, float b) { return a + b; }
+__device__ __forceinline__ float xmax16_32(float v) { return xpair32(xpair16(v, fmax_op), fmax_op); }
+__device__ __forceinline__ float xsum16_32(float v) { return xpair32(xpair16(v, add_op), add_op); }
 
 // Row of the permuted 16-key score tile t (0/1) that lane row m loads:
 // keys 8*(m/4) + m%4 for tile 0 and 8*(m/4) + 4 + m%4 for tile 1, so the C
@@ -966,9 +974,18 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) tmin = min(tmin, __shfl_xor(tmin, o));
   tmin = __builtin_amdgcn_readfirstlane(tmin);
+  // Low-rank A-operand rows: stacked row k = 16 mb + n holds rank k when
+  // k < r. With r < 16 the row k = r is all bf16 ones, so its accumulator
+  // entry collects each query row's softmax denominator from the same bf16 P.
+  const bool ones_row = p.r < 16;
   uint32_t lr_mask[MB];
+  u32x4 lr_ones[MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) lr_mask[mb] = mb * 16 + n < p.r ? 0xffffffffu : 0u;
+  for (int mb = 0; mb < MB; ++mb) {
+    lr_mask[mb] = mb * 16 + n < p.r ? 0xffffffffu : 0u;
+    const uint32_t one = ones_row && mb * 16 + n == p.r ? 0x3f803f80u : 0u;
+    lr_ones[mb] = u32x4{one, one, one, one};
+  }
 
   float m_run[RB], l_run[RB];
   f32x4 oacc[RB][DB], lacc[RB][MB];
@@ -1031,89 +1048,90 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
     const int vbase = own ? b : 0;                       // view position of segment key 0
     const int seg_lim = own ? S : b;                     // keys beyond the segment are invalid
     const u16* kv = s_kv + buf * PE;
+    // S^T = K Q^T for the page's 64 keys and the RB row blocks, one 16-key
+    // score tile (half h, tile t: index 2h + t) at a time
+    f32x4 sacc[RB][4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int key0 = pg_key0 + h * 32;
-      // every row of the wave sees all 32 keys of this half
-      const bool whole = key0 + 32 <= seg_lim && vbase + key0 + 31 <= tmin;
-      // S^T = K Q^T for the RB row blocks, one 16-key score tile at a time
-      f32x4 sacc[RB][2];
+    for (int ht = 0; ht < 4; ++ht) {
+      bf16x8 kf[KS];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        bf16x8 kf[KS];
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          kf[s] = *reinterpret_cast<const bf16x8*>(kv + ((h * 2 + t) * KS + s) * 512 + lane * 8);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          f32x4 acc = {0, 0, 0, 0};
-#pragma unroll
-          for (int s = 0; s < KS; ++s) acc = mfma(kf[s], qf[rb][s], acc);
-          sacc[rb][t] = acc;
-        }
-      }
-      // online softmax per row block; P^T stays in registers as the B operand
-      bf16x8 pt[RB];
+      for (int s = 0; s < KS; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(kv + (ht * KS + s) * 512 + lane * 8);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        float sc[8];
-        if (whole) {
+        f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            sc[jj] = sacc[rb][0][jj] * p.scale_log2;
-            sc[jj + 4] = sacc[rb][1][jj] * p.scale_log2;
-          }
-        } else {
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int kA = key0 + 8 * q + jj, kB = kA + 4;
-            const bool okA = kA < seg_lim && vbase + kA <= tpos[rb];
-            const bool okB = kB < seg_lim && vbase + kB <= tpos[rb];
-            sc[jj] = okA ? sacc[rb][0][jj] * p.scale_log2 : -INFINITY;
-            sc[jj + 4] = okB ? sacc[rb][1][jj] * p.scale_log2 : -INFINITY;
-          }
-        }
-        float mx = sc[0];
-#pragma unroll
-        for (int j2 = 1; j2 < 8; ++j2) mx = fmaxf(mx, sc[j2]);
-        mx = xmax16_32(mx);
-        const float m_new = fmaxf(m_run[rb], mx);
-        float pv[8], ps = 0.f;
-#pragma unroll
-        for (int j2 = 0; j2 < 8; ++j2) {
-          pv[j2] = __builtin_amdgcn_exp2f(sc[j2] - m_new);
-          ps += pv[j2];
-        }
-        // rescale the accumulators only when some row's running max grew
-        // (rare once the maxima settle); otherwise the scale factor is 1
-        if (__any(m_new > m_run[rb])) {
-          const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
-          l_run[rb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) oacc[rb][db] *= alpha;
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) lacc[rb][mb] *= alpha;
-          m_run[rb] = m_new;
-        }
-        l_run[rb] += ps;
-        pt[rb] = pack8(pv);
-      }
-      // O^T += V^T P^T and L^T += LR^T P^T, one operand tile at a time
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(kv + 64 * D + (h * DB + db) * 512 + lane * 8);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma(vf, pt[rb], oacc[rb][db]);
-      }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int k = min(mb * 16 + n, p.r - 1);
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(kv + 2 * 64 * D + k * kPage + h * 32 + 8 * q);
-        const bf16x8 lf = __builtin_bit_cast(bf16x8, raw & lr_mask[mb]);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) lacc[rb][mb] = mfma(lf, pt[rb], lacc[rb][mb]);
+        for (int s = 0; s < KS; ++s) acc = mfma(kf[s], qf[rb][s], acc);
+        sacc[rb][ht] = acc;
       }
     }
+    // every row of the wave sees all 64 keys of the page
+    const bool whole = pg_key0 + 64 <= seg_lim && vbase + pg_key0 + 63 <= tmin;
+    // Online softmax over the page per row block. Lane (n, q) holds keys
+    // 32h + 8q + 4t + j (score i = 8h + 4t + j), which in half h is the
+    // B-operand slice P^T needs. Scores are scaled inside the exponent's FMA;
+    // the running max is kept in the scaled (log2) domain.
+    bf16x8 pt[RB][2];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float sc[16];
+      if (whole) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[i] = sacc[rb][i >> 2][i & 3];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = pg_key0 + 32 * (i >> 3) + 8 * q + (i & 7);
+          sc[i] = key < seg_lim && vbase + key <= tpos[rb] ? sacc[rb][i >> 2][i & 3] : -INFINITY;
+        }
+      }
+      float mx = sc[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+      mx = xmax16_32(mx);
+      const float m_new = fmaxf(m_run[rb], mx * p.scale_log2);
+      float pv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], p.scale_log2, -m_new));
+      // rescale the accumulators only when some row's running max grew
+      // (rare once the maxima settle); otherwise the scale factor is 1
+      if (__any(m_new > m_run[rb])) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[rb][db] *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) lacc[rb][mb] *= alpha;
+        m_run[rb] = m_new;
+      }
+      if (!ones_row) {
+        float ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ps += pv[i];
+        l_run[rb] += ps;
+      }
+      pt[rb][0] = pack8(pv);
+      pt[rb][1] = pack8(pv + 8);
+    }
+    // O^T += V^T P^T and L^T += LR^T P^T, one operand tile at a time; with a
+    // spare low-rank row, that row is all ones and accumulates the row sums
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(kv + 64 * D + (h * DB + db) * 512 + lane * 8);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma(vf, pt[rb][h], oacc[rb][db]);
+      }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = min(mb * 16 + n, p.r - 1);
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(kv + 2 * 64 * D + k * kPage + h * 32 + 8 * q);
+        const bf16x8 lf = __builtin_bit_cast(bf16x8, (raw & lr_mask[mb]) | lr_ones[mb]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) lacc[rb][mb] = mfma(lf, pt[rb][h], lacc[rb][mb]);
+      }
     __builtin_amdgcn_s_waitcnt(kWaitOnePage);  // this wave's copies of page i + 1 have landed
     __builtin_amdgcn_s_barrier();              // ... and every other wave's; buffer i % 3 is free
   }
@@ -1125,7 +1143,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
   const u16* Bi = p.B + (uint64_t)p.ag_id[ai] * p.r * HD + g * D;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const float l = xsum16_32(l_run[rb]);
+    // denominator: the ones row's entry (lane (n, r / 4), entry 0 since r is a
+    // multiple of 4), else the lanes' partial sums
+    const float l = ones_row ? __shfl(lacc[rb][0][0], n + 4 * p.r) : xsum16_32(l_run[rb]);
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
