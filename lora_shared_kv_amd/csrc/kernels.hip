@@ -101,6 +101,25 @@ __device__ __forceinline__ float add_op(float a, float b) { return a + b; }
 __device__ __forceinline__ float xmax16_32(float v) { return xpair32(xpair16(v, fmax_op), fmax_op); }
 __device__ __forceinline__ float xsum16_32(float v) { return xpair32(xpair16(v, add_op), add_op); }
 
+// Whole-wave reductions without LDS: DPP quad permutes (lanes xor 1, xor 2),
+// the 8-lane and 16-lane mirrors (which pair the halves of each group), then
+// the two permlane swaps. Every lane ends with the result.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+  v = op(v, dppf<0xb1>(v));   // quad_perm [1, 0, 3, 2]
+  v = op(v, dppf<0x4e>(v));   // quad_perm [2, 3, 0, 1]
+  v = op(v, dppf<0x141>(v));  // row_half_mirror
+  v = op(v, dppf<0x140>(v));  // row_mirror
+  v = xpair16(v, op);
+  return xpair32(v, op);
+}
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, fmax_op); }
+__device__ __forceinline__ float wave_sum(float v) { return wave_reduce(v, add_op); }
+
 // Row of the permuted 16-key score tile t (0/1) that lane row m loads:
 // keys 8*(m/4) + m%4 for tile 0 and 8*(m/4) + 4 + m%4 for tile 1, so the C
 // tile entry j of lane group q is key 8q + j (tile 0) or 8q + 4 + j (tile 1).
@@ -820,12 +839,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
                               (e - p.D) * kPage + p.new_slot[a]]);
   }
   // --- softmax statistics
-  float M = m_s;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  float M = wave_max(m_s);
   if (p.step && w == 0) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
+    dot = wave_sum(dot);
     if (lane == 0) s_new = dot * p.scale_log2;
   }
   if (lane == 0) s_m[w] = M;
@@ -841,8 +857,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
     s_w[s] = e;
     L += e * slot_row(s)[E + 1];
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+  L = wave_sum(L);
   if (lane == 0) s_l[w] = L;
   __syncthreads();
   const float e_new = p.step ? __builtin_amdgcn_exp2f(m_new - M) : 0.f;
