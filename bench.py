@@ -157,6 +157,14 @@ def main():
     arena = torch.empty(B.skv_arena_bytes(c), dtype=torch.uint8, device=dev)
     ctx = B.skv_create(c, arena, stream)
 
+    # measured ceilings on this machine (reported beside the vendor peaks): a
+    # streaming read over 2 GiB (well past the 256 MB infinity cache) and a
+    # dense bf16 MFMA issue loop
+    probe_buf = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    stream_gbs = B.skv_probe_stream_read(probe_buf, reps=5)
+    del probe_buf
+    mfma_tflops = B.skv_probe_mfma_bf16()
+
     gen = torch.Generator(device=dev)
     gen.manual_seed(1003)
 
@@ -242,6 +250,8 @@ def main():
         traffic = load_traffic("decode_split_traffic.json")
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "measured_peak": round(stream_gbs, 1),
+                    "frac_of_measured": round(achieved / stream_gbs, 4),
                     "kernel": "decode_split_kernel<128,1,1>",
                     "algorithmic_bytes_per_launch": int(bytes_avg),
                     "avg_launch_us": round(avg_split_s * 1e6, 3)}
@@ -269,7 +279,8 @@ def main():
         fl = prefill_flops(Hq, d, r, [prefix + Ssuf] * N, [prefill_n] * N)
         tf = fl / (pms / 1e3 / pn) / 1e12
         prefill = {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                   "frac": round(tf / BF16_PEAK_TFLOPS, 4), "kernel": "prefill_kernel<128,1>",
+                   "frac": round(tf / BF16_PEAK_TFLOPS, 4), "kernel": "prefill_kernel<128,1,2,8>",
+                   "measured_peak": round(mfma_tflops, 1), "frac_of_measured": round(tf / mfma_tflops, 4),
                    "flops_per_launch": fl, "avg_launch_ms": round(pms / pn, 4),
                    "ms_all_layers": round(pms, 3), "n_q_per_agent": prefill_n,
                    "view": prefix + Ssuf}

@@ -237,6 +237,20 @@ int skv_sync(skv_ctx* ctx);
 /* Message of the last failed call on ctx ("" if none). */
 const char* skv_last_error(const skv_ctx* ctx);
 
+/* Measurement probes (no context; the current device; synchronous on
+ * `stream`, a hipStream_t, 0 = default). They calibrate the rooflines the
+ * attention kernels are reported against and are not part of the path.
+ * skv_probe_stream_read: reads the device buffer src (bytes: a multiple of 16,
+ *   at least 1 MiB; caller-owned, contents irrelevant) once per repetition
+ *   with non-temporal 16-byte loads from every CU; *gbs = the best of `reps`
+ *   repetitions in GB/s (10^9 bytes/s).
+ * skv_probe_mfma_bf16: a dense v_mfma_f32_16x16x32_bf16 issue loop, two waves
+ *   per SIMD on every CU with independent accumulators; *tflops = the
+ *   achieved dense bf16 rate (10^12 flop/s, 2 flops per multiply-add).
+ * Errors: ARG (NULL pointers, bad sizes), HIP, UNSUPPORTED (CPU-only build). */
+int skv_probe_stream_read(const void* src, uint64_t bytes, int reps, void* stream, double* gbs);
+int skv_probe_mfma_bf16(void* stream, double* tflops);
+
 #ifdef __cplusplus
 }
 #endif

@@ -84,5 +84,8 @@ int dev_sync(const Geometry& g);
 int dev_set_timing(Geometry& g, int mask);
 int dev_collect_timing(Geometry& g, skv_kernel_times* out);
 const char* dev_last_error();
+// measurement probes (no context): see skv_probe_stream_read / skv_probe_mfma_bf16
+int dev_probe_stream_read(const void* src, uint64_t bytes, int reps, void* stream, double* gbs);
+int dev_probe_mfma_bf16(void* stream, double* tflops);
 
 }  // namespace skv

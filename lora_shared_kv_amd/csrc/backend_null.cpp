@@ -36,5 +36,7 @@ int dev_collect_timing(Geometry&, skv_kernel_times* out) {
   return SKV_OK;
 }
 const char* dev_last_error() { return ""; }
+int dev_probe_stream_read(const void*, uint64_t, int, void*, double*) { return SKV_ERR_UNSUPPORTED; }
+int dev_probe_mfma_bf16(void*, double*) { return SKV_ERR_UNSUPPORTED; }
 
 }  // namespace skv

@@ -41,6 +41,12 @@
 
 #include "backend.h"
 
+namespace skv {
+// Written by the probe kernels only on an impossible value; external linkage,
+// so the compiler must keep the work that feeds it.
+__device__ unsigned int probe_sink[4];
+}  // namespace skv
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -1200,6 +1206,45 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Measurement probes (roofline calibration; not part of the attention path)
+// ---------------------------------------------------------------------------
+
+
+// Grid-stride non-temporal 16-byte reads, eight in flight per lane.
+__global__ __launch_bounds__(256) void probe_stream_kernel(const u32x4* __restrict__ src, size_t n) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  u32x4 acc = {0, 0, 0, 0};
+  for (; i + 7 * stride < n; i += 8 * stride) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u];
+  }
+  for (; i < n; i += stride) acc ^= __builtin_nontemporal_load(src + i);
+  if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x9e3779b9u) skv::probe_sink[threadIdx.x & 3] = acc[0];
+}
+
+// Back-to-back v_mfma_f32_16x16x32_bf16 on eight independent accumulators.
+__global__ __launch_bounds__(256) void probe_mfma_kernel(int iters) {
+  const uint32_t lane = threadIdx.x & 63;
+  const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{0x3a003a00u + lane, 0x3a003a00u, 0x3a003a00u, 0x3a003a00u});
+  const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{0x3a003a00u, 0x3a003a00u + lane, 0x3a003a00u, 0x3a003a00u});
+  f32x4 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0, 0, 0, 0};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = mfma(a, b, acc[j]);
+  }
+  f32x4 t = acc[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) t += acc[j];
+  if (t[0] + t[1] + t[2] + t[3] == 1234.5f) skv::probe_sink[threadIdx.x & 3] = __float_as_uint(t[0]);
+}
+
+// ---------------------------------------------------------------------------
 // Host side: launch helpers, planning, timing
 // ---------------------------------------------------------------------------
 
@@ -1509,6 +1554,51 @@ static_assert(sizeof(DecodeParams) <= 4096, "kernel arguments too large");
 static_assert(sizeof(MergeParams) <= 4096, "kernel arguments too large");
 static_assert(sizeof(AppendParams) <= 4096, "kernel arguments too large");
 static_assert(sizeof(PrefillParams) <= 4096, "kernel arguments too large");
+
+// Time `reps` launches of a probe with dispatch events; return the shortest
+// interval in milliseconds (or a negative HIP error).
+template <typename Kernel, typename... Args>
+static double probe_best_ms(hipStream_t st, int reps, dim3 grid, Kernel kernel, Args... args) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return -1.0;
+  double best = 1e30;
+  for (int r = 0; r < reps; ++r) {
+    hipExtLaunchKernelGGL(kernel, grid, dim3(256), 0, st, a, b, 0, args...);
+    if (hipGetLastError() != hipSuccess || hipEventSynchronize(b) != hipSuccess) {
+      best = -1.0;
+      break;
+    }
+    float ms = 0.f;
+    (void)hipEventElapsedTime(&ms, a, b);
+    best = std::min(best, (double)ms);
+  }
+  (void)hipEventDestroy(a);
+  (void)hipEventDestroy(b);
+  return best;
+}
+
+int dev_probe_stream_read(const void* src, uint64_t bytes, int reps, void* stream, double* gbs) {
+  const double ms = probe_best_ms((hipStream_t)stream, reps, dim3(16384), probe_stream_kernel,
+                                  (const u32x4*)src, (size_t)(bytes / 16));
+  if (ms <= 0) {
+    set_err("probe_stream_kernel", hipGetLastError());
+    return SKV_ERR_HIP;
+  }
+  *gbs = (double)bytes / (ms * 1e-3) / 1e9;
+  return SKV_OK;
+}
+
+int dev_probe_mfma_bf16(void* stream, double* tflops) {
+  constexpr int kIters = 2048, kBlocks = 2 * kCUs;  // two waves per SIMD
+  const double ms = probe_best_ms((hipStream_t)stream, 3, dim3(kBlocks), probe_mfma_kernel, kIters);
+  if (ms <= 0) {
+    set_err("probe_mfma_kernel", hipGetLastError());
+    return SKV_ERR_HIP;
+  }
+  const double flops = (double)kBlocks * 4 * kIters * 8 * (16.0 * 16 * 32 * 2);
+  *tflops = flops / (ms * 1e-3) / 1e12;
+  return SKV_OK;
+}
 
 int dev_attn_decode(const Geometry& g, const AttnJob& job) { return decode_impl(g, job, nullptr); }
 

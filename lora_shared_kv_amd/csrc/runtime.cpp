@@ -649,4 +649,14 @@ int skv_sync(skv_ctx* c) {
 
 const char* skv_last_error(const skv_ctx* c) { return c ? c->err.c_str() : "null context"; }
 
+int skv_probe_stream_read(const void* src, uint64_t bytes, int reps, void* stream, double* gbs) {
+  if (!src || !gbs || bytes < (1u << 20) || bytes % 16 || reps < 1) return SKV_ERR_ARG;
+  return skv::dev_probe_stream_read(src, bytes, reps, stream, gbs);
+}
+
+int skv_probe_mfma_bf16(void* stream, double* tflops) {
+  if (!tflops) return SKV_ERR_ARG;
+  return skv::dev_probe_mfma_bf16(stream, tflops);
+}
+
 }  // extern "C"

@@ -69,6 +69,8 @@ EXPORTS = {
     "skv_collect_timing": (_I, [_P, ctypes.POINTER(skv_kernel_times)]),
     "skv_sync": (_I, [_P]),
     "skv_last_error": (ctypes.c_char_p, [_P]),
+    "skv_probe_stream_read": (_I, [_P, ctypes.c_uint64, _I, _P, ctypes.POINTER(ctypes.c_double)]),
+    "skv_probe_mfma_bf16": (_I, [_P, ctypes.POINTER(ctypes.c_double)]),
 }
 
 _LIBS = {}
@@ -317,3 +319,34 @@ def skv_sync(ctx: Ctx):
 
 def skv_last_error(ctx: Ctx) -> str:
     return ctx.lib.skv_last_error(ctx.handle).decode()
+
+
+def _stream_handle(stream):
+    """hipStream_t of a torch.cuda.Stream, a raw int, or None (torch's current stream)."""
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(stream if isinstance(stream, int) else stream.cuda_stream)
+
+
+def skv_probe_stream_read(buf, reps: int = 5, stream=None) -> float:
+    """Streaming-read bandwidth (GB/s) over a device buffer (a CUDA tensor)."""
+    lib = load_library("gpu")
+    out = ctypes.c_double()
+    nbytes = buf.numel() * buf.element_size()
+    rc = lib.skv_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes - nbytes % 16, int(reps),
+                                   _stream_handle(stream), ctypes.byref(out))
+    if rc != 0:
+        raise RuntimeError(f"skv_probe_stream_read failed: {_CODES.get(rc, rc)}")
+    return out.value
+
+
+def skv_probe_mfma_bf16(stream=None) -> float:
+    """Dense bf16 MFMA rate (TFLOP/s) of a back-to-back issue loop."""
+    lib = load_library("gpu")
+    out = ctypes.c_double()
+    rc = lib.skv_probe_mfma_bf16(_stream_handle(stream), ctypes.byref(out))
+    if rc != 0:
+        raise RuntimeError(f"skv_probe_mfma_bf16 failed: {_CODES.get(rc, rc)}")
+    return out.value
+

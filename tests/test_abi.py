@@ -12,7 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     src = open(os.path.join(ROOT, "include", "skv.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    names = set(re.findall(r"\b(skv_[a-z_]+)\s*\(", src))
+    names = set(re.findall(r"\b(skv_[a-z0-9_]+)\s*\(", src))
     return sorted(names)
 
 
