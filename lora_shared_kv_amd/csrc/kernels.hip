@@ -83,6 +83,15 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// max of three floats in one instruction. fmaxf would first quiet each
+// operand that could be a signalling NaN (one extra instruction per operand);
+// the scores here are finite or -inf.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ bf16x8 pack8(const float* p) {
   bf16x8 r;
 #pragma unroll
@@ -922,12 +931,19 @@ struct PrefillParams {
 template <int D>
 constexpr int prefill_page_elems() { return 2 * 64 * D + 32 * 64; }
 
-// Copy one 1 KB operand block from global memory into LDS: every lane moves
-// 16 bytes, lane l landing at dst + 16 l (the DMA places a wave's data
-// contiguously from the LDS base it is given).
-__device__ __forceinline__ void dma_block(const u16* src_wave, u16* dst_wave, int lane) {
-  __builtin_amdgcn_global_load_lds((const void*)(src_wave + lane * 8),
-                                   (void __attribute__((address_space(3)))*)dst_wave, 16, 0, 0);
+// Copy one 1 KB operand block into LDS with a buffer load that writes LDS:
+// every lane moves 16 bytes from byte offset off + 16 lane of the buffer,
+// landing at dst + 16 lane (the data of a wave is placed contiguously from the
+// LDS base it is given). Reads past the buffer's size return zeros. A buffer
+// load counts only in the vector-memory counter, so waits for LDS reads that
+// follow it stay exact.
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit records
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+}
+__device__ __forceinline__ void dma_block(__amdgpu_buffer_rsrc_t r, int off, u16* dst_wave, int lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)dst_wave, 16, off + lane * 16,
+                                           0, 0, 0);
 }
 
 // Suffix prefill: a workgroup of NW waves takes 16 NW RB query rows (rows =
@@ -999,6 +1015,11 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
   // k < r. With r < 16 the row k = r is all bf16 ones, so its accumulator
   // entry collects each query row's softmax denominator from the same bf16 P.
   const bool ones_row = p.r < 16;
+  // The score scale in a VGPR, read here once: a value the compiler would
+  // reload from the kernel arguments inside the page loop would leave a
+  // scalar load in flight there, and every LDS wait would then count to zero.
+  float scale_log2 = p.scale_log2;
+  asm volatile("" : "+v"(scale_log2));
   uint32_t lr_mask[MB];
   u32x4 lr_ones[MB];
 #pragma unroll
@@ -1023,99 +1044,222 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
 
   const uint64_t head_off = (uint64_t)g * kPage * D;
   const uint64_t page_elems = (uint64_t)p.Hkv * kPage * D;
-  // The workgroup's copy of page i into LDS buffer buf: each wave moves KB of
-  // the K tile's 1 KB blocks, as many of the V^T tile's, and one 1 KB block
-  // of low-rank rows (waves past the page's block count repeat block 0, the
-  // same bytes to the same place), so every wave issues the same number of
-  // copies (kCopies) and the wait below can count them. With r = 4 the block
-  // runs 512 bytes past the page's rows, inside the arena; those rows are never
-  // read.
-  auto copy_page = [&](int i, int buf) {
-    const int page = s_pages[i];
-    const u16* kp = p.K + (uint64_t)page * page_elems + head_off;
-    const u16* vp = p.VT + (uint64_t)page * page_elems + head_off;
-    u16* dst = s_kv + buf * PE;
-#pragma unroll
-    for (int u = 0; u < KB; ++u) {
-      const int blk = w * KB + u;
-      dma_block(kp + blk * 512, dst + blk * 512, lane);
-      dma_block(vp + blk * 512, dst + 64 * D + blk * 512, lane);
-    }
-    const int lb = w < lr_blocks ? w : 0;
-    dma_block(lrb + (uint64_t)page * p.r * kPage + lb * 512, dst + 2 * 64 * D + lb * 512, lane);
+  // Page copies into LDS are issued by the first wave group (waves [0, NW/2)):
+  // each of its waves moves KC of the K tile's 1 KB blocks, as many of the
+  // V^T tile's, and the low-rank block w (waves past the page's block count
+  // repeat block 0, the same bytes to the same place). With r = 4 the second
+  // half of that block lies past the page's rows and lands as zeros; it is
+  // never read.
+  constexpr int NG = NW / 2;       // waves per group
+  constexpr int KC = D / 8 / NG;   // 1 KB blocks of a K (or V^T) tile per copying wave
+  static_assert(KC * NG * 8 == D, "page tile blocks must split evenly over a wave group");
+  constexpr int NC = 2 * KC + 1;   // copies one copying wave issues per page
+  const int lb = w < lr_blocks ? w : 0;
+  struct PageSrc {
+    __amdgpu_buffer_rsrc_t k, v, l;
   };
-  constexpr int kCopies = 2 * KB + 1;  // copies one wave issues per page
-  // s_waitcnt with only vmcnt limited (expcnt and lgkmcnt at their maxima)
-  constexpr int kWaitOnePage = (kCopies & 15) | ((kCopies >> 4) << 14) | (7 << 4) | (15 << 8);
+  auto page_src = [&](int page) {
+    return PageSrc{byte_rsrc(p.K + (uint64_t)page * page_elems + head_off, 64 * D * 2),
+                   byte_rsrc(p.VT + (uint64_t)page * page_elems + head_off, 64 * D * 2),
+                   byte_rsrc(lrb + (uint64_t)page * p.r * kPage, p.r * kPage * 2)};
+  };
+  auto copy_one = [&](int c, const PageSrc& src, u16* dst) {
+    if (c < KC) {
+      const int blk = w * KC + c;
+      dma_block(src.k, blk * 1024, dst + blk * 512, lane);
+    } else if (c < 2 * KC) {
+      const int blk = w * KC + c - KC;
+      dma_block(src.v, blk * 1024, dst + 64 * D + blk * 512, lane);
+    } else {
+      dma_block(src.l, lb * 1024, dst + 2 * 64 * D + lb * 512, lane);
+    }
+  };
+  auto copy_page = [&](int page, int buf) {
+    const PageSrc src = page_src(page);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) copy_one(c, src, s_kv + buf * PE);
+  };
+  // s_waitcnt for every vector-memory operation of the wave (expcnt and
+  // lgkmcnt left at their maxima)
+  constexpr int kWaitCopies = (7 << 4) | (15 << 8);
+  // s_waitcnt for every LDS and scalar-memory operation (vmcnt and expcnt at
+  // their maxima)
+  constexpr int kWaitLgkm = 15 | (7 << 4) | (3 << 14);
 
-  // Ring of three page buffers: page i is computed from buffer i % 3 while the
-  // copies of pages i + 1 and i + 2 are in flight. Before the barrier that
-  // publishes page i + 1, each wave waits until only its copies of page i + 2
-  // are outstanding; buffer (i + 2) % 3 was last read in iteration i - 1,
-  // before the previous barrier. The page list is clamped at the end, so every
-  // iteration issues one page of copies (the surplus ones are never read).
-  auto clampi = [&](int i) { return min(i, n_pages - 1); };
-  if (n_pages > 0) {
-    copy_page(0, 0);
-    copy_page(clampi(1), 1);
-    __builtin_amdgcn_s_waitcnt(kWaitOnePage);
-    __builtin_amdgcn_s_barrier();
+  // Two wave groups, waves [0, NW/2) and [NW/2, NW): wave w and wave w + NW/2
+  // run on the same SIMD. Each wave alternates an MFMA phase (O^T, L^T += the
+  // previous page's V^T P^T, LR^T P^T; then S^T = K Q^T for the next page) with a
+  // softmax phase (the page's P from S). The second group runs one phase behind
+  // the first, so on every SIMD one wave issues MFMAs while the other works on
+  // the vector ALU and the exponential unit; a barrier separates the phases.
+  //
+  // Page j sits in LDS buffer j % 3. The first group reads it in phases 2j and
+  // 2j + 2, the second in phases 2j + 1 and 2j + 3. The first group issues the
+  // copy of page j + 1 inside its MFMA phase 2j (the buffer last held page
+  // j - 2, read for the last time in phase 2j - 1) and waits for it at the end
+  // of phase 2j + 1.
+  const bool lead = w < NG;
+  f32x4 sacc[RB][4];
+  bf16x8 pt[RB][2];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sacc[rb][t] = f32x4{0, 0, 0, 0};
+    pt[rb][0] = pt[rb][1] = bf16x8{};
   }
-  for (int i = 0; i < n_pages; ++i) {
-    const int buf = i % 3;
-    copy_page(clampi(i + 2), (i + 2) % 3);
+
+  // MFMA phase j for the first and the last page: the V^T and low-rank
+  // products of page j - 1 (from its P), then the scores of page j
+  auto mfma_phase = [&](int j) {
+    if (j >= 1) {
+      const u16* kv = s_kv + ((j - 1) % 3) * PE;
+      // O^T += V^T P^T and L^T += LR^T P^T; with a spare low-rank row, that
+      // row is all ones and accumulates the row sums
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(kv + 64 * D + (h * DB + db) * 512 + lane * 8);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma(vf, pt[rb][h], oacc[rb][db]);
+        }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int k = min(mb * 16 + n, p.r - 1);
+          const u32x4 raw = *reinterpret_cast<const u32x4*>(kv + 2 * 64 * D + k * kPage + h * 32 + 8 * q);
+          const bf16x8 lf = __builtin_bit_cast(bf16x8, (raw & lr_mask[mb]) | lr_ones[mb]);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) lacc[rb][mb] = mfma(lf, pt[rb][h], lacc[rb][mb]);
+        }
+    }
+    if (j < n_pages) {
+      const u16* kv = s_kv + (j % 3) * PE;
+      // S^T = K Q^T for the page's 64 keys and the RB row blocks, one 16-key
+      // score tile (half h, tile t: index 2h + t) at a time
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) {
+        bf16x8 kf[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(kv + (ht * KS + s) * 512 + lane * 8);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) acc = mfma(kf[s], qf[rb][s], acc);
+          sacc[rb][ht] = acc;
+        }
+      }
+    }
+  };
+
+  // The same MFMA phase for 1 <= j < n_pages, as one sequence of NF operand
+  // fragments (V^T tiles, low-rank rows, K tiles), each feeding RB MFMAs. A
+  // wave reads LDS at a bounded rate (about 32 bytes a clock), so the first PF
+  // V^T tiles of page j - 1 are read during the wave's softmax phase of that
+  // page (which uses no LDS) into vpre; the rest are read kAhead fragments
+  // before their use, starting with the first MFMA, so that the wave's reads
+  // run during the whole phase and their latency hides behind the MFMAs of
+  // the fragments before them. With
+  // WC set, the copies of the page src into buffer dst ride along, one per
+  // fragment.
+  constexpr int NV = 2 * DB, NL = 2 * MB, NK = 4 * KS, NF = NV + NL + NK;
+  constexpr int PF = NV / 2;
+  constexpr int kAhead = PF;  // reads in flight: at most 15 are counted
+  static_assert(NC <= NF, "copies ride along the fragments");
+  static_assert(PF % RB == 0 && kAhead <= 15, "prefetch split");
+  bf16x8 vpre[PF];
+  auto frag_load = [&](int f, const u16* kvp, const u16* kvc) -> bf16x8 {
+    if (f < NV)  // V^T tile: half h = f / DB, column block db = f % DB
+      return *reinterpret_cast<const bf16x8*>(kvp + 64 * D + f * 512 + lane * 8);
+    if (f < NV + NL) {  // low-rank rows: block mb, half h
+      const int mb = (f - NV) >> 1, h = (f - NV) & 1;
+      const int k = min(mb * 16 + n, p.r - 1);
+      return *reinterpret_cast<const bf16x8*>(kvp + 2 * 64 * D + k * kPage + h * 32 + 8 * q);
+    }
+    // K tile (ht, s), taken chunk-major (s outer) so that consecutive MFMAs
+    // update different score tiles
+    const int ks = f - NV - NL, ht = ks % 4, s = ks / 4;
+    return *reinterpret_cast<const bf16x8*>(kvc + (ht * KS + s) * 512 + lane * 8);
+  };
+  auto frag_use = [&](int f, bf16x8 x) {
+    if (f < NV) {
+      const int h = f / DB, db = f % DB;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma(x, pt[rb][h], oacc[rb][db]);
+    } else if (f < NV + NL) {
+      const int mb = (f - NV) >> 1, h = (f - NV) & 1;
+      const bf16x8 lf = __builtin_bit_cast(bf16x8, (__builtin_bit_cast(u32x4, x) & lr_mask[mb]) | lr_ones[mb]);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) lacc[rb][mb] = mfma(lf, pt[rb][h], lacc[rb][mb]);
+    } else {
+      const int ks = f - NV - NL, ht = ks % 4, s = ks / 4;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) sacc[rb][ht] = mfma(x, qf[rb][s], s == 0 ? f32x4{0, 0, 0, 0} : sacc[rb][ht]);
+    }
+  };
+  auto mfma_phase_full = [&](int j, auto wc, int src_page, int dst_buf) {
+    constexpr bool WC = decltype(wc)::value;
+    const u16* kvp = s_kv + ((j - 1) % 3) * PE;
+    const u16* kvc = s_kv + (j % 3) * PE;
+    PageSrc src{};
+    if (WC) src = page_src(src_page);
+    u16* dst = s_kv + dst_buf * PE;
+    bf16x8 fr[NF];
+#pragma unroll
+    for (int f = 0; f < PF; ++f) fr[f] = vpre[f];
+    // program order is kept (sched_barrier) so that the reads leave in the
+    // order of use and each wait covers just the fragment needed
+#pragma unroll
+    for (int f = PF; f < kAhead && f < NF; ++f) {
+      fr[f] = frag_load(f, kvp, kvc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int g = f + kAhead;
+      if (g >= PF && g < NF) fr[g] = frag_load(g, kvp, kvc);
+      frag_use(f, fr[f]);
+      if (WC && f < NC) copy_one(f, src, dst);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Softmax phase of page i: online softmax per row block. Lane (n, q) holds
+  // keys 32h + 8q + 4t + j (score i = 8h + 4t + j), which in half h is the
+  // B-operand slice P^T needs. Scores are scaled inside the exponent's FMA and
+  // the running max m is kept in the scaled (log2) domain. m is raised only
+  // when some score exceeds it by more than kSlack (then the accumulators are
+  // rescaled), so P stays below 2^kSlack and a page needs no cross-lane
+  // reduction unless its max grows that far; the normalisation at the end
+  // divides by the sum of the same P, so the result does not depend on m.
+  constexpr float kSlack = 8.f;
+  auto softmax_phase = [&](int i) {
+    const u16* kvi = s_kv + (i % 3) * PE + 64 * D;  // V^T tile of page i
     const bool own = i >= np_sh;
     const int pg_key0 = (own ? i - np_sh : i) * kPage;  // first key of the page in its segment
     const int vbase = own ? b : 0;                       // view position of segment key 0
     const int seg_lim = own ? S : b;                     // keys beyond the segment are invalid
-    const u16* kv = s_kv + buf * PE;
-    // S^T = K Q^T for the page's 64 keys and the RB row blocks, one 16-key
-    // score tile (half h, tile t: index 2h + t) at a time
-    f32x4 sacc[RB][4];
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
-      bf16x8 kf[KS];
-#pragma unroll
-      for (int s = 0; s < KS; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(kv + (ht * KS + s) * 512 + lane * 8);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        f32x4 acc = {0, 0, 0, 0};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) acc = mfma(kf[s], qf[rb][s], acc);
-        sacc[rb][ht] = acc;
-      }
-    }
     // every row of the wave sees all 64 keys of the page
     const bool whole = pg_key0 + 64 <= seg_lim && vbase + pg_key0 + 63 <= tmin;
-    // Online softmax over the page per row block. Lane (n, q) holds keys
-    // 32h + 8q + 4t + j (score i = 8h + 4t + j), which in half h is the
-    // B-operand slice P^T needs. Scores are scaled inside the exponent's FMA;
-    // the running max is kept in the scaled (log2) domain.
-    bf16x8 pt[RB][2];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      float sc[16];
-      if (whole) {
+      if (!whole) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sc[i] = sacc[rb][i >> 2][i & 3];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = pg_key0 + 32 * (i >> 3) + 8 * q + (i & 7);
-          sc[i] = key < seg_lim && vbase + key <= tpos[rb] ? sacc[rb][i >> 2][i & 3] : -INFINITY;
+        for (int e = 0; e < 16; ++e) {
+          const int key = pg_key0 + 32 * (e >> 3) + 8 * q + (e & 7);
+          if (!(key < seg_lim && vbase + key <= tpos[rb])) sacc[rb][e >> 2][e & 3] = -INFINITY;
         }
       }
-      float mx = sc[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
-      mx = xmax16_32(mx);
-      const float m_new = fmaxf(m_run[rb], mx * p.scale_log2);
-      float pv[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], p.scale_log2, -m_new));
-      // rescale the accumulators only when some row's running max grew
-      // (rare once the maxima settle); otherwise the scale factor is 1
-      if (__any(m_new > m_run[rb])) {
+      // max over the lane's 16 scores as a tree (short dependency chain)
+      const f32x4* sa = sacc[rb];
+      const float m0 = max3f(sa[0][0], sa[0][1], sa[0][2]), m1 = max3f(sa[0][3], sa[1][0], sa[1][1]);
+      const float m2 = max3f(sa[1][2], sa[1][3], sa[2][0]), m3 = max3f(sa[2][1], sa[2][2], sa[2][3]);
+      const float m4 = max3f(sa[3][0], sa[3][1], sa[3][2]);
+      const float mx = max3f(max3f(m0, m1, m2), max3f(m3, m4, sa[3][3]), -INFINITY);
+      if (__any(mx * scale_log2 > m_run[rb] + kSlack)) {
+        const float m_new = fmaxf(m_run[rb], xmax16_32(mx) * scale_log2);
         const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
         l_run[rb] *= alpha;
 #pragma unroll
@@ -1124,39 +1268,90 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
         for (int mb = 0; mb < MB; ++mb) lacc[rb][mb] *= alpha;
         m_run[rb] = m_new;
       }
+      // this row block's share of the V^T prefetch, each read followed by a
+      // few of the exponentials' instructions (a wave's LDS reads issue at a
+      // bounded rate, so a burst of them would stall the wave)
+      constexpr int PV = PF / RB;
+#pragma unroll
+      for (int f = rb * PV; f < (rb + 1) * PV; ++f) vpre[f] = *reinterpret_cast<const bf16x8*>(kvi + f * 512 + lane * 8);
+      float pv[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rb][e >> 2][e & 3], scale_log2, -m_run[rb]));
+#pragma unroll
+      for (int f = 0; f < PV; ++f) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
       if (!ones_row) {
         float ps = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ps += pv[i];
+        for (int e = 0; e < 16; ++e) ps += pv[e];
         l_run[rb] += ps;
       }
       pt[rb][0] = pack8(pv);
       pt[rb][1] = pack8(pv + 8);
     }
-    // O^T += V^T P^T and L^T += LR^T P^T, one operand tile at a time; with a
-    // spare low-rank row, that row is all ones and accumulates the row sums
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(kv + 64 * D + (h * DB + db) * 512 + lane * 8);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma(vf, pt[rb][h], oacc[rb][db]);
-      }
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int k = min(mb * 16 + n, p.r - 1);
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(kv + 2 * 64 * D + k * kPage + h * 32 + 8 * q);
-        const bf16x8 lf = __builtin_bit_cast(bf16x8, (raw & lr_mask[mb]) | lr_ones[mb]);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) lacc[rb][mb] = mfma(lf, pt[rb][h], lacc[rb][mb]);
-      }
-    __builtin_amdgcn_s_waitcnt(kWaitOnePage);  // this wave's copies of page i + 1 have landed
-    __builtin_amdgcn_s_barrier();              // ... and every other wave's; buffer i % 3 is free
+    // the prefetched tiles have landed long before the phase ends; waiting
+    // for them here keeps the count of LDS reads in flight in the MFMA phase
+    // within what the counter tracks
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+  };
+
+  using CopyOn = std::integral_constant<bool, true>;
+  using CopyOff = std::integral_constant<bool, false>;
+  if (lead) {
+    if (n_pages > 0) copy_page(s_pages[0], 0);
+    if (n_pages > 1) copy_page(s_pages[1], 1);
   }
-  __builtin_amdgcn_s_waitcnt(0);  // surplus copies of the last iterations
+  __builtin_amdgcn_s_waitcnt(kWaitCopies);
+  __builtin_amdgcn_s_barrier();
+  // Iteration j holds phases 2j and 2j + 1, each closed by a barrier; the
+  // groups run separate loops so that each keeps its phase order fixed. The
+  // first iteration has no products of a previous page and the last no
+  // scores, so both are peeled off the steady loops.
+  if (n_pages > 0) {
+    if (lead) {
+      mfma_phase(0);
+      __builtin_amdgcn_s_barrier();
+      int pid = s_pages[min(2, n_pages - 1)];
+      softmax_phase(0);
+      int next_page = __builtin_amdgcn_readfirstlane(pid);  // the page the next iteration copies
+      // nothing of the prologue stays in flight on the LDS/scalar counter,
+      // so the waits inside the loop can count LDS reads alone
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+      __builtin_amdgcn_s_barrier();
+      for (int j = 1; j < n_pages; ++j) {
+        // at j = n_pages - 1 this copies the last page once more into the
+        // free buffer n_pages % 3 (it held page n_pages - 3); it is never read
+        mfma_phase_full(j, CopyOn{}, next_page, (j + 1) % 3);
+        __builtin_amdgcn_s_barrier();
+        pid = s_pages[min(j + 2, n_pages - 1)];
+        softmax_phase(j);
+        next_page = __builtin_amdgcn_readfirstlane(pid);
+        __builtin_amdgcn_s_waitcnt(kWaitCopies);  // this wave's copies of page j + 1 have landed
+        __builtin_amdgcn_s_barrier();             // ... and every other wave's
+      }
+      mfma_phase(n_pages);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_s_barrier();
+    } else {
+      __builtin_amdgcn_s_barrier();
+      mfma_phase(0);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+      __builtin_amdgcn_s_barrier();
+      for (int j = 1; j < n_pages; ++j) {
+        softmax_phase(j - 1);
+        __builtin_amdgcn_s_barrier();
+        mfma_phase_full(j, CopyOff{}, 0, 0);
+        __builtin_amdgcn_s_barrier();
+      }
+      softmax_phase(n_pages - 1);
+      __builtin_amdgcn_s_barrier();
+      mfma_phase(n_pages);
+      __builtin_amdgcn_s_barrier();
+    }
+  }
   __syncthreads();
 
   // finalize: o = (oacc + lacc . B_i) / l, B_i applied once for the block's rows
