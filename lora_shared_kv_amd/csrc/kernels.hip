@@ -13,9 +13,11 @@
 //                       wavefront shuffles. Writes partial (m, l, o, o_lr).
 //   decode_merge_kernel merges the partials of one (agent, KV head), then
 //                       applies B_i once: o += (P V_lr) B_i[:, g*d:(g+1)*d].
-//   prefill_kernel      one workgroup per (KV head, agent, 128 query rows):
+//   prefill_kernel      one workgroup per (KV head, agent, 256 query rows):
 //                       the same MFMA tile scheme over the agent's whole view
-//                       with a causal mask, B_i applied once per query block.
+//                       with a causal mask, pages staged in LDS for the whole
+//                       workgroup, two wave groups alternating MFMA and
+//                       softmax phases; B_i applied once per query row.
 //
 // The method (LRAgent review, "What carries the argument"): V_i = V_base +
 // (X A_i) B_i is never formed; attention computes O = P V_base + (P V_lr) B_i.
