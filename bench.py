@@ -22,6 +22,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -65,8 +66,14 @@ def prefill_flops(Hq, d, r, views, n_q):
 
 
 def kernel_hash():
+    """Hash of the kernel source's code with comments and blank lines removed, so
+    that a comment edit does not orphan counters taken on the same code."""
     p = os.path.join(ROOT, "lora_shared_kv_amd", "csrc", "kernels.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    src = open(p).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    code = "\n".join(l.rstrip() for l in src.splitlines() if l.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def load_traffic(name):
