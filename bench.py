@@ -138,6 +138,13 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-events", action="store_true",
                     help="time the decode steps without per-launch HIP events (no roofline)")
+    ap.add_argument("--layout", default="shared", choices=["shared", "private"],
+                    help="shared: the prefix once, in SHARED pages (the method); private: every agent "
+                         "holds its own copy of the prefix in its own pages (the Non-Shared comparison)")
+    ap.add_argument("--adapters", default=None, choices=["BaseShared", "BaseLRShared"],
+                    help="adapter mode instead of the workload's (BaseShared: one A_i per agent)")
+    ap.add_argument("--ttft", action="store_true",
+                    help="also time one new agent's first token: its rows and prefill on every layer")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
     args = ap.parse_args()
@@ -151,11 +158,18 @@ def main():
 
     cfg = WORKLOADS[args.workload]
     L, Hq, Hkv, d, hidden, r, N, mode, prefix = cfg
+    if args.adapters:
+        mode = 1 if args.adapters == "BaseLRShared" else 0
+    private = args.layout == "private"
+    default_run = not private and mode == cfg[7]
     G = Hq // Hkv
     total_steps = args.warmup + args.steps
     prefill_n = 512
     own_max = args.warmup + 2 * args.steps + (0 if args.no_prefill else prefill_n)
-    max_pages = prefix // 64 + 1 + N * (own_max // 64 + 2) + 4
+    if private:
+        max_pages = N * ((prefix + own_max) // 64 + 2) + 4
+    else:
+        max_pages = prefix // 64 + 1 + N * (own_max // 64 + 2) + 4
     c = dict(n_layers=L, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, hidden=hidden, rank=r,
              n_agents=N, mode=mode, page_size=64, max_pages=max_pages)
     dev = torch.device("cuda", 0)
@@ -181,19 +195,39 @@ def main():
             t.mul_(var ** 0.5)
         return t.to(torch.bfloat16)
 
-    # ---- setup: shared prefix (base K/V + low-rank rows with the shared A) ----
-    A = randn(hidden, r, var=1.0 / hidden)
+    # ---- setup: the prefix's base K/V and low-rank rows, once in SHARED pages
+    # (shared layout) or once per agent in its own pages (private layout) ----
+    A = randn(N, hidden, r, var=1.0 / hidden) if mode == 0 else randn(hidden, r, var=1.0 / hidden)
+    A_of = (lambda a: A[a].contiguous()) if mode == 0 else (lambda a: A)
+    plane_of = (lambda a: a) if mode == 0 else (lambda a: 0)
     Bw = randn(N, r, Hkv * d, var=0.01 / r)
     chunk = 8192
     xbuf = randn(chunk, hidden)
     for l in range(L):
         for lo in range(0, prefix, chunk):
             n = min(chunk, prefix - lo)
-            B.skv_append_base(ctx, l, -1, randn(n, Hkv, d), randn(n, Hkv, d))
-            B.skv_append_lowrank(ctx, l, -1, 0, n, xbuf[:n].contiguous(), A)
-    for a in range(N):
-        B.skv_crop(ctx, a, prefix)
+            k_rows, v_rows = randn(n, Hkv, d), randn(n, Hkv, d)
+            x_rows = xbuf[:n].contiguous()
+            if private:
+                # the same context rows in every agent's own pages, each with its own adapter
+                for a in range(N):
+                    B.skv_append_base(ctx, l, a, k_rows, v_rows)
+                    B.skv_append_lowrank(ctx, l, a, plane_of(a), n, x_rows, A_of(a))
+            else:
+                B.skv_append_base(ctx, l, -1, k_rows, v_rows)
+                for pl in (range(N) if mode == 0 else [0]):
+                    B.skv_append_lowrank(ctx, l, -1, pl, n, x_rows, A_of(pl))
+    if not private:
+        for a in range(N):
+            B.skv_crop(ctx, a, prefix)
     B.skv_sync(ctx)
+    base0, own0 = (0, prefix) if private else (prefix, 0)
+    cnt = B.skv_get_counters(ctx)
+    page_kv = 64 * 4 * Hkv * d  # K and V bytes of one page of one layer
+    memory = {"kv_pages": int(cnt["pages_alloc"] - cnt["pages_freed"]),
+              "kv_bytes": int((cnt["pages_alloc"] - cnt["pages_freed"]) * page_kv),
+              "lr_rows": int(cnt["lr_rows"]), "lr_bytes": int(cnt["lr_rows"]) * 2 * r,
+              "arena_bytes": int(arena.numel())}
     agents = list(range(N))
     kin = [randn(N, Hkv, d) for _ in range(L)]
     vin = [randn(N, Hkv, d) for _ in range(L)]
@@ -207,9 +241,9 @@ def main():
     Ap, Bp = A.data_ptr(), Bw.data_ptr()
     ag = B.int_array(agents)
     ones = B.int_array([1] * N)
-    bl = B.int_array([prefix] * N)
-    sl = B.int_array([0] * N)
-    S = [0] * N
+    bl = B.int_array([base0] * N)
+    sl = B.int_array([own0] * N)
+    S = [own0] * N
 
     def step():
         # one fused decode step per layer: append each agent's new row, attend
@@ -250,7 +284,7 @@ def main():
     split_ms, split_n = times.get("decode_split", (0.0, 0))
     roofline = None
     if split_n:
-        bytes_avg = sum(decode_split_bytes(Hkv, d, r, hidden, prefix, [s] * N, N, Hq)
+        bytes_avg = sum(decode_split_bytes(Hkv, d, r, hidden, base0, [s] * N, N, Hq, bls=mode == 1)
                         for s in suffix_hist) / len(suffix_hist)
         avg_split_s = split_ms / 1e3 / split_n
         achieved = bytes_avg / avg_split_s / 1e9
@@ -279,18 +313,48 @@ def main():
         B.skv_set_timing(ctx, True)
         B.skv_collect_timing(ctx)
         for l in range(L):
-            B.skv_attn_prefill(ctx, l, agents, [prefix] * N, [Ssuf] * N, [prefill_n] * N, qp, Bw, op)
+            B.skv_attn_prefill(ctx, l, agents, [base0] * N, [Ssuf] * N, [prefill_n] * N, qp, Bw, op)
         pt = B.skv_collect_timing(ctx)
         B.skv_set_timing(ctx, False)
         pms, pn = pt["prefill"]
-        fl = prefill_flops(Hq, d, r, [prefix + Ssuf] * N, [prefill_n] * N)
+        fl = prefill_flops(Hq, d, r, [base0 + Ssuf] * N, [prefill_n] * N)
         tf = fl / (pms / 1e3 / pn) / 1e12
         prefill = {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                    "frac": round(tf / BF16_PEAK_TFLOPS, 4), "kernel": "prefill_kernel<128,1,2,8>",
                    "measured_peak": round(mfma_tflops, 1), "frac_of_measured": round(tf / mfma_tflops, 4),
                    "flops_per_launch": fl, "avg_launch_ms": round(pms / pn, 4),
                    "ms_all_layers": round(pms, 3), "n_q_per_agent": prefill_n,
-                   "view": prefix + Ssuf}
+                   "view": base0 + Ssuf}
+        S = [Ssuf] * N
+
+    # ---- time to first token of one new agent (agent 0 starts over): its rows
+    # and its prefill on every layer, then one decode step. Shared layout: its
+    # 512-token suffix over the cached prefix. Private layout: it must first
+    # build its own copy of the prefix, so its rows and queries cover the whole
+    # context ----
+    ttft = None
+    if args.ttft:
+        a0 = [0]
+        n_new = prefill_n + (prefix if private else 0)
+        B.skv_crop(ctx, 0, 0 if private else prefix)
+        B.skv_sync(ctx)
+        kt, vt, xt = randn(n_new, Hkv, d), randn(n_new, Hkv, d), randn(n_new, hidden)
+        qt = randn(n_new, Hq, d)
+        ot = torch.empty_like(qt)
+        k1, v1, x1, q1 = randn(1, Hkv, d), randn(1, Hkv, d), randn(1, hidden), randn(1, Hq, d)
+        o1 = torch.empty_like(q1)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for l in range(L):
+            for lo in range(0, n_new, chunk):
+                n = min(chunk, n_new - lo)
+                B.skv_append_agents(ctx, l, a0, [n], kt[lo:lo + n], vt[lo:lo + n], xt[lo:lo + n], A)
+            B.skv_attn_prefill(ctx, l, a0, [base0], [n_new], [n_new], qt, Bw, ot)
+        for l in range(L):
+            B.skv_decode_step(ctx, l, a0, [base0], [n_new], k1, v1, x1, A, q1, Bw, o1)
+        torch.cuda.synchronize()
+        ttft = {"ms": round(1e3 * (time.perf_counter() - t0), 3), "rows_appended_per_layer": n_new + 1,
+                "queries_prefilled_per_layer": n_new}
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -305,15 +369,19 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "layers": L, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": d, "hidden": hidden, "rank": r, "agents": N,
-                   "mode": "BaseLRShared" if mode == 1 else "BaseShared", "shared_prefix": prefix,
+                   "mode": "BaseLRShared" if mode == 1 else "BaseShared",
+                   "layout": args.layout, "shared_prefix": prefix,
                    "decode_tokens_per_step": N, "global_batch": N, "seq_len": prefix,
                    "parallelism": "single-gpu"},
         "roofline": roofline,
         "kernels": per_kernel,
         "prefill": prefill,
+        "memory": memory,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if ttft is not None:
+        res["ttft"] = ttft
+    if not args.no_cpu_baseline and default_run:
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
     print(json.dumps(res), flush=True)
 

@@ -195,6 +195,25 @@ def test_edge_cases(name, shape, prefix, own, kw):
     R.run_parity(sc, log=lambda m: log(f"[{name}] {m}"))
 
 
+@pytest.mark.parametrize("shape_name", ["llama3", "qwen3"])
+def test_private_prefix_layout(shape_name):
+    """The comparison layout in which every agent holds its own copy of the
+    context in its own pages (b_i = 0, no shared rows): a 64-query prefill,
+    then fused decode steps."""
+    R = _runner()
+    shape = synth.WORKLOADS[shape_name]
+    sc = synth.Schedule(shape, 1011, n_layers=1)
+    sc.draw_adapters()
+    agents = list(range(shape.n_agents))
+    sc.own_rows(0, agents, [2048] * len(agents))
+    sc.attend("prefill", 0, agents, [64] * len(agents), tag="private prefill")
+    for t in range(3):
+        sc.decode_step(0, agents, tag=f"private step {t}")
+    assert sc.b == [0] * shape.n_agents
+    _, _, res = R.run_parity(sc, log=log)
+    assert len(res) == 4
+
+
 def test_lr_only_term():
     """V_base = 0: the output is only (P V_lr) B_i, about 10x smaller than usual."""
     R = _runner()

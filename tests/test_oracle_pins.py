@@ -377,6 +377,40 @@ def test_planted_mistake_is_caught(name, monkeypatch):
 # state-model error semantics
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("mode", [BASE_SHARED, BASE_LR_SHARED])
+def test_private_copies_equal_shared_prefix(mode):
+    """The comparison layout in which every agent holds its own copy of the
+    context in its own pages attends over the same rows as the shared prefix
+    followed by the agent's suffix, so the outputs agree (the LRAgent review
+    compares both layouts; only where the rows live differs)."""
+    rng = np.random.default_rng(41)
+    hq, hkv, d, r, N, hidden, P, own = 6, 2, 64, 4, 2, 64, 9, 3
+    planes = N if mode == BASE_SHARED else 1
+    A = rng.standard_normal((planes, hidden, r)) / math.sqrt(hidden)
+    B = rng.standard_normal((N, r, hkv * d)) * 0.3
+    k, v = rng.standard_normal((P, hkv, d)), rng.standard_normal((P, hkv, d))
+    x = rng.standard_normal((P, hidden))
+    ko, vo = rng.standard_normal((N, own, hkv, d)), rng.standard_normal((N, own, hkv, d))
+    xo = rng.standard_normal((N, own, hidden))
+    sh = CacheModel(1, hq, hkv, d, hidden, r, N, mode, 4, 256)
+    pv = CacheModel(1, hq, hkv, d, hidden, r, N, mode, 4, 256)
+    sh.append_base(0, SHARED, k, v)
+    for p in range(planes):
+        sh.append_lowrank(0, SHARED, p, P, x, A[p])
+    for a in range(N):
+        pl = sh.plane_of(a)
+        sh.crop(a, P)
+        sh.append_base(0, a, ko[a], vo[a])
+        sh.append_lowrank(0, a, pl, own, xo[a], A[pl])
+        pv.append_base(0, a, np.concatenate([k, ko[a]]), np.concatenate([v, vo[a]]))
+        pv.append_lowrank(0, a, pl, P + own, np.concatenate([x, xo[a]]), A[pl])
+    assert pv.base_len == [0] * N and sh.base_len == [P] * N
+    q = rng.standard_normal((N * own, hq, d))
+    o_sh = oracle.attention_outputs(sh, 0, list(range(N)), [own] * N, q, B)
+    o_pv = oracle.attention_outputs(pv, 0, list(range(N)), [own] * N, q, B)
+    assert np.allclose(o_sh, o_pv, rtol=RTOL, atol=RTOL)
+
+
 def test_errors_leave_state_unchanged():
     c = CacheModel(1, 4, 2, 64, 64, 4, 2, BASE_SHARED, 4, 3)
     k = np.zeros((9, 2, 64))
