@@ -173,6 +173,17 @@ int skv_decode_step(skv_ctx* ctx, int layer, int n, const int* agents, const int
                     const skv_bf16* x, const skv_bf16* A, const skv_bf16* q, const skv_bf16* B,
                     skv_bf16* o);
 
+/* Adapter activation offset of one agent (RoleKV, "What it does": an
+ * activated adapter switches on after the role's header, and everything
+ * before it is processed with the base weights; "Challenges we ran into": the
+ * offset is passed explicitly). From the next attention call on, view
+ * positions j < pos of the agent take no low-rank term:
+ * V_i[j] = V_base[j] + [j >= pos] (X_j A) B_i. The rows stay cached (in
+ * BaseLRShared they are the shared plane's rows other agents use). 0 (the
+ * default) turns the adapter on everywhere; pos may lie beyond the view.
+ * Host metadata only. Errors: ARG (agent out of range, pos < 0). */
+int skv_set_lr_begin(skv_ctx* ctx, int agent, int pos);
+
 /* a7: set a view length on every layer (RoleKV "How we built it": crop at a
  * handoff; paperlayer Sec. 2: takeover boundary). Host metadata only.
  *   seq = agent i with no own rows and new_len >= b_i: (re)attach, b_i = new_len

@@ -58,6 +58,7 @@ struct AppendJob {
 
 struct AttnAgent {
   int32_t agent, b, S, plane, n_q, q_row0;
+  int32_t lr_begin;  // view positions below it take no low-rank term
 };
 
 struct AttnJob {

@@ -94,6 +94,15 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return r;
 }
 
+// Zero the first nm of the eight bf16 values of x (value 2k is the low half
+// of 32-bit word k). nm <= 0 keeps all of them, nm >= 8 zeroes all.
+__device__ __forceinline__ bf16x8 zero_leading(bf16x8 x, int nm) {
+  u32x4 u = __builtin_bit_cast(u32x4, x);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) u[k] &= (2 * k < nm ? 0u : 0x0000ffffu) | (2 * k + 1 < nm ? 0u : 0xffff0000u);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
 __device__ __forceinline__ bf16x8 pack8(const float* p) {
   bf16x8 r;
 #pragma unroll
@@ -495,6 +504,8 @@ struct DecodeParams {
   int ag_b[SKV_MAX_AGENTS];
   int ag_S[SKV_MAX_AGENTS];
   int ag_pidx[SKV_MAX_AGENTS];    // index of the agent's plane in planes[]
+  int ag_lrb[SKV_MAX_AGENTS];     // adapter activation offset (view position)
+  int lr_offsets;                 // some agent of the group has a nonzero offset
   int n_planes;
   int planes[SKV_MAX_AGENTS];     // stacked low-rank planes of this group
   int seg_off[SKV_MAX_AGENTS + 1];  // flattened offset of each own suffix; seg_off[n] = total
@@ -546,7 +557,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 
   // per-lane query rows: Q^T B-operand slices, agent and base length of the row
   bf16x8 qf[RB][KS];
-  int row_agent[RB], row_b[RB], row_S[RB];
+  int row_agent[RB], row_b[RB], row_S[RB], row_lrb[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int rho = rb * 16 + n;
@@ -555,6 +566,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     row_agent[rb] = ok ? a : -1;
     row_b[rb] = ok ? p.ag_b[a] : 0;
     row_S[rb] = ok ? p.ag_S[a] : 0;
+    row_lrb[rb] = ok ? p.ag_lrb[a] : 0;
     const u16* qp = p.q + ((uint64_t)a * p.Hq + g * p.G + rho % p.G) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[rb][s] = ok ? ld8(qp + 32 * s + 8 * q) : zero8();
@@ -663,9 +675,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
       const bf16x8 pt = pack8(pv);
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[rb][db] = mfma(ch.v[db], pt, oacc[rb][db]);
+      // keys of the lane's eight that lie before its row's adapter activation
+      // (view position: the shared key, or b_i + own key) take no low-rank term
+      bf16x8 ptl = pt;
+      if (p.lr_offsets) {
+        const int nm = row_lrb[rb] - (seg == 0 ? 0 : row_b[rb]) - key0 - 8 * q;
+        if (__any(nm > 0)) ptl = zero_leading(pt, nm);
+      }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-        lacc[rb][mb] = mfma(__builtin_bit_cast(bf16x8, ch.l[mb] & lr_mask[mb]), pt, lacc[rb][mb]);
+        lacc[rb][mb] = mfma(__builtin_bit_cast(bf16x8, ch.l[mb] & lr_mask[mb]), ptl, lacc[rb][mb]);
     }
   };
   const int n_chunks = w < n_ck ? (n_ck - w + 3) / 4 : 0;  // this wave's chunks: w, w + 4, ...
@@ -781,6 +800,7 @@ struct MergeParams {
   const u16* LRT;     // layer base of plane 0 (holds the new low-rank rows)
   uint64_t lr_plane;
   int new_page[SKV_MAX_AGENTS], new_slot[SKV_MAX_AGENTS], plane[SKV_MAX_AGENTS];
+  int new_lr_on[SKV_MAX_AGENTS];  // the new token lies at or after the agent's adapter activation
   float scale_log2;
   int n_rows;       // leading blocks merge rows; the n_app after them copy the new K/V rows
   int n_app;
@@ -852,8 +872,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
   if (p.step && threadIdx.x < E) {
     const int e = threadIdx.x;
     nv = e < p.D ? bf2f(p.v_new[((uint64_t)a * p.Hkv + g) * p.D + e])
-                 : bf2f(p.LRT[(uint64_t)p.plane[a] * p.lr_plane + (uint64_t)p.new_page[a] * p.r * kPage +
-                              (e - p.D) * kPage + p.new_slot[a]]);
+         : !p.new_lr_on[a] ? 0.f
+                           : bf2f(p.LRT[(uint64_t)p.plane[a] * p.lr_plane + (uint64_t)p.new_page[a] * p.r * kPage +
+                                        (e - p.D) * kPage + p.new_slot[a]]);
   }
   // --- softmax statistics
   float M = wave_max(m_s);
@@ -924,6 +945,7 @@ struct PrefillParams {
   int n;
   int ag_id[SKV_MAX_AGENTS], ag_b[SKV_MAX_AGENTS], ag_S[SKV_MAX_AGENTS];
   int ag_plane[SKV_MAX_AGENTS], ag_nq[SKV_MAX_AGENTS], ag_row0[SKV_MAX_AGENTS];
+  int ag_lrb[SKV_MAX_AGENTS];    // adapter activation offset (view position)
   int blk0[SKV_MAX_AGENTS + 1];  // prefix sums of query blocks per agent
   float scale_log2;
 };
@@ -956,7 +978,7 @@ __device__ __forceinline__ void dma_block(__amdgpu_buffer_rsrc_t r, int off, u16
 // so one K/V tile read serves RB row blocks. Scores stay in registers as in
 // decode (S^T = K Q^T with permuted K rows); causal and segment masks are
 // applied per key, except on 32-key halves every row of the wave sees whole.
-template <int D, int MB, int RB, int NW>
+template <int D, int MB, int RB, int NW, bool LRO>
 __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
   constexpr int KS = D / 32, DB = D / 16;
   constexpr int ROWS = NW * 16 * RB;
@@ -1030,6 +1052,21 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
     const uint32_t one = ones_row && mb * 16 + n == p.r ? 0x3f803f80u : 0u;
     lr_ones[mb] = u32x4{one, one, one, one};
   }
+
+  // With LRO (some agent has an adapter activation offset), the low-rank rows
+  // of keys before the agent's offset are masked out of the A operand; the
+  // ones row is added after the mask, so the denominators still see every key.
+  // lr_keep(i, h): mask of the lane's eight keys of page i, half h.
+  const int lr_on_at = p.ag_lrb[ai];
+  auto lr_keep = [&](int i, int h) -> u32x4 {
+    const int pstart = i >= np_sh ? b + (i - np_sh) * kPage : i * kPage;  // view position of the page
+    const int nm = lr_on_at - (pstart + 32 * h + 8 * q);
+    u32x4 m;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m[k] = (2 * k < nm ? 0u : 0x0000ffffu) | (2 * k + 1 < nm ? 0u : 0xffff0000u);
+    return m;
+  };
+  u32x4 keep_lr[2] = {u32x4{~0u, ~0u, ~0u, ~0u}, u32x4{~0u, ~0u, ~0u, ~0u}};
 
   float m_run[RB], l_run[RB];
   f32x4 oacc[RB][DB], lacc[RB][MB];
@@ -1131,7 +1168,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
         for (int h = 0; h < 2; ++h) {
           const int k = min(mb * 16 + n, p.r - 1);
           const u32x4 raw = *reinterpret_cast<const u32x4*>(kv + 2 * 64 * D + k * kPage + h * 32 + 8 * q);
-          const bf16x8 lf = __builtin_bit_cast(bf16x8, (raw & lr_mask[mb]) | lr_ones[mb]);
+          const u32x4 keep = LRO ? lr_keep(j - 1, h) : u32x4{~0u, ~0u, ~0u, ~0u};
+          const bf16x8 lf = __builtin_bit_cast(bf16x8, (raw & lr_mask[mb] & keep) | lr_ones[mb]);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) lacc[rb][mb] = mfma(lf, pt[rb][h], lacc[rb][mb]);
         }
@@ -1192,7 +1230,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
       for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma(x, pt[rb][h], oacc[rb][db]);
     } else if (f < NV + NL) {
       const int mb = (f - NV) >> 1, h = (f - NV) & 1;
-      const bf16x8 lf = __builtin_bit_cast(bf16x8, (__builtin_bit_cast(u32x4, x) & lr_mask[mb]) | lr_ones[mb]);
+      const bf16x8 lf =
+          __builtin_bit_cast(bf16x8, (__builtin_bit_cast(u32x4, x) & lr_mask[mb] & keep_lr[h]) | lr_ones[mb]);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) lacc[rb][mb] = mfma(lf, pt[rb][h], lacc[rb][mb]);
     } else {
@@ -1203,6 +1242,10 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
   };
   auto mfma_phase_full = [&](int j, auto wc, int src_page, int dst_buf) {
     constexpr bool WC = decltype(wc)::value;
+    if (LRO) {
+      keep_lr[0] = lr_keep(j - 1, 0);
+      keep_lr[1] = lr_keep(j - 1, 1);
+    }
     const u16* kvp = s_kv + ((j - 1) % 3) * PE;
     const u16* kvc = s_kv + (j % 3) * PE;
     PageSrc src{};
@@ -1524,20 +1567,25 @@ constexpr int kPrefNW = 8;
 constexpr int kPrefRB = 2;
 constexpr int prefill_rows(int) { return kPrefNW * 16 * kPrefRB; }
 
-template <int D, int MB>
+template <int D, int MB, bool LRO>
 int launch_prefill(const skv::Geometry& g, const PrefillParams& p, int blocks) {
   const size_t lds = (size_t)3 * prefill_page_elems<D>() * sizeof(u16);
   // the page ring exceeds the default dynamic LDS limit (set once per process;
   // the attribute holds for every device)
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(prefill_kernel<D, MB, kPrefRB, kPrefNW>),
+      reinterpret_cast<const void*>(prefill_kernel<D, MB, kPrefRB, kPrefNW, LRO>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) {
     set_err("hipFuncSetAttribute(prefill_kernel)", attr);
     return SKV_ERR_HIP;
   }
-  return launch(g, 4, prefill_kernel<D, MB, kPrefRB, kPrefNW>, dim3(blocks), lds, p, "prefill_kernel",
+  return launch(g, 4, prefill_kernel<D, MB, kPrefRB, kPrefNW, LRO>, dim3(blocks), lds, p, "prefill_kernel",
                 64 * kPrefNW);
+}
+
+template <int D, int MB>
+int launch_prefill_o(const skv::Geometry& g, const PrefillParams& p, int blocks, bool lro) {
+  return lro ? launch_prefill<D, MB, true>(g, p, blocks) : launch_prefill<D, MB, false>(g, p, blocks);
 }
 
 template <int D>
@@ -1645,6 +1693,8 @@ static int decode_impl(const Geometry& g, const AttnJob& job, const AppendJob* a
         p.planes[p.n_planes++] = a.plane;
       }
       p.ag_pidx[i] = pidx;
+      p.ag_lrb[i] = a.lr_begin;
+      if (a.lr_begin > 0) p.lr_offsets = 1;
       max_b = std::max(max_b, a.b);
     }
     // A fused step writes the group's new rows: the low-rank rows (and new
@@ -1734,6 +1784,8 @@ static int decode_impl(const Geometry& g, const AttnJob& job, const AppendJob* a
         mp.new_page[i] = app->ids[sp.ids_off];
         mp.new_slot[i] = sp.pos0 % kPage;
         mp.plane[i] = sp.plane;
+        const AttnAgent& ag = job.ag[a0 + i];
+        mp.new_lr_on[i] = ag.b + ag.S >= ag.lr_begin;  // the new token's view position
       }
       mp.scale_log2 = p.scale_log2;
       mp.app = kv_app;
@@ -1835,14 +1887,17 @@ int dev_attn_prefill(const Geometry& g, const AttnJob& job) {
     p.ag_plane[i] = a.plane;
     p.ag_nq[i] = a.n_q;
     p.ag_row0[i] = a.q_row0;
+    p.ag_lrb[i] = a.lr_begin;
     p.blk0[i + 1] = p.blk0[i] + (a.n_q * g.G + rows - 1) / rows;
   }
   p.scale_log2 = 1.4426950408889634f / sqrtf((float)g.D);
   const int blocks = p.blk0[job.n] * g.Hkv;
   if (blocks == 0) return SKV_OK;
+  bool lro = false;  // some agent's adapter activation offset lies inside its view
+  for (int i = 0; i < job.n; ++i) lro |= job.ag[i].lr_begin > 0;
   if (g.D == 128)
-    return mb == 1 ? launch_prefill<128, 1>(g, p, blocks) : launch_prefill<128, 2>(g, p, blocks);
-  return mb == 1 ? launch_prefill<64, 1>(g, p, blocks) : launch_prefill<64, 2>(g, p, blocks);
+    return mb == 1 ? launch_prefill_o<128, 1>(g, p, blocks, lro) : launch_prefill_o<128, 2>(g, p, blocks, lro);
+  return mb == 1 ? launch_prefill_o<64, 1>(g, p, blocks, lro) : launch_prefill_o<64, 2>(g, p, blocks, lro);
 }
 
 int dev_sync(const Geometry& g) {

@@ -88,6 +88,7 @@ struct skv_ctx {
   Geometry g{};
   std::vector<Layer> layers;
   std::vector<int> base_len;
+  std::vector<int> lr_begin;  // per agent: first view position with the adapter term on
   skv_counters counters{};
   std::string err;
 
@@ -208,6 +209,7 @@ int skv_create(const skv_config* cfg, void* dev_arena, size_t arena_bytes, void*
     l.lr_own.assign(g.N, 0);
   }
   c->base_len.assign(g.N, 0);
+  c->lr_begin.assign(g.N, 0);
   *out = c;
   return SKV_OK;
 }
@@ -412,7 +414,7 @@ static int validate_attend(skv_ctx* c, int layer, int n, const int* agents, cons
     int p = c->plane_of(a);
     if (l.lr_shared[p] < b || l.lr_own[a] < S)
       return c->fail(SKV_ERR_STATE, "agent %d: low-rank rows do not cover the view", a);
-    job.ag[i] = skv::AttnAgent{a, b, S, p, nq, row};
+    job.ag[i] = skv::AttnAgent{a, b, S, p, nq, row, c->lr_begin[a]};
     row += nq;
   }
   job.q = (const uint16_t*)q;
@@ -479,7 +481,7 @@ int skv_decode_step(skv_ctx* c, int layer, int n, const int* agents, const int* 
       return c->fail(SKV_ERR_STATE, "agent %d low-rank rows (%d) lag base rows (%d)", a, l.lr_own[a], S);
     if (l.lr_shared[p] < b)
       return c->fail(SKV_ERR_STATE, "agent %d: low-rank rows do not cover the view", a);
-    job.ag[i] = skv::AttnAgent{a, b, S, p, 1, i};
+    job.ag[i] = skv::AttnAgent{a, b, S, p, 1, i, c->lr_begin[a]};
     need += ceil_div(S + 1, g.ps) - (int)l.tbl[1 + a].size();
   }
   if (need > (int)l.free.size())
@@ -538,6 +540,14 @@ int skv_decode_step(skv_ctx* c, int layer, int n, const int* agents, const int* 
   c->counters.pages_alloc += (int64_t)taken.size();
   c->counters.base_rows_own += n;
   (x ? c->counters.lr_rows : c->counters.lr_zero_rows) += n;
+  return SKV_OK;
+}
+
+int skv_set_lr_begin(skv_ctx* c, int agent, int pos) {
+  if (!c) return SKV_ERR_ARG;
+  if (agent < 0 || agent >= c->g.N) return c->fail(SKV_ERR_ARG, "agent id %d", agent);
+  if (pos < 0) return c->fail(SKV_ERR_ARG, "negative activation offset %d", pos);
+  c->lr_begin[agent] = pos;
   return SKV_OK;
 }
 

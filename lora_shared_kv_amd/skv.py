@@ -61,6 +61,7 @@ EXPORTS = {
     "skv_attn_decode": (_I, [_P, _I, _I, _IP, _IP, _IP, _P, _P, _P]),
     "skv_decode_step": (_I, [_P, _I, _I, _IP, _IP, _IP, _P, _P, _P, _P, _P, _P, _P]),
     "skv_crop": (_I, [_P, _I, _I]),
+    "skv_set_lr_begin": (_I, [_P, _I, _I]),
     "skv_get_lens": (_I, [_P, _I, _IP, _IP, _IP, _IP, _IP]),
     "skv_get_pages": (_I, [_P, _I, _I, ctypes.POINTER(ctypes.c_int32), _I]),
     "skv_get_pools": (_I, [_P, ctypes.POINTER(skv_pools)]),
@@ -262,6 +263,10 @@ def skv_decode_step(ctx: Ctx, layer: int, agents, base_len, suffix_len, k, v, x,
 
 def skv_crop(ctx: Ctx, seq: int, new_len: int):
     ctx._check(ctx.lib.skv_crop(ctx.handle, seq, new_len))
+
+
+def skv_set_lr_begin(ctx: Ctx, agent: int, pos: int):
+    ctx._check(ctx.lib.skv_set_lr_begin(ctx.handle, agent, pos))
 
 
 def skv_get_lens(ctx: Ctx, layer: int) -> dict:

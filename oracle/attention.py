@@ -11,7 +11,9 @@ reordered or fused:
   1. V_i[j, g, :] = V_base[j, g, :] + (X_j A) B_i[:, g*d:(g+1)*d]
      (the LoRA value projection Y = X W0 + (X A) B, the review's statement of
      the paper's Eq. 3; B_i is r x (Hkv*d) and column slice g belongs to KV
-     head g).
+     head g). With an activation offset t_i for agent i (RoleKV, "What it
+     does": the adapter switches on after the role's header), the term is
+     present only for j >= t_i.
   2. For a query at view position t and query head h, with KV head
      g = floor(h / G) (G = Hq / Hkv; the pages do not say how query heads map
      to KV heads, the reading taken is contiguous groups):
@@ -89,6 +91,8 @@ def attention_outputs(cache, layer, agents, n_q, q, b_all, rows=None):
         idx = [i for i in range(nq) if off + i in want]
         if idx:
             k, vb, lr = cache.view(layer, a)
+            lr = lr.copy()
+            lr[:cache.lr_begin[a]] = 0.0  # positions before the adapter's activation
             L = k.shape[0]
             v = materialize_values(vb, lr, b_all[a])
             pos = [L - nq + i for i in idx]

@@ -97,6 +97,10 @@ class CacheModel:
         self.tables = [{s: [] for s in seqs} for _ in range(n_layers)]
         self.length = [{s: 0 for s in seqs} for _ in range(n_layers)]
         self.base_len = [0] * n_agents
+        # view position from which each agent's adapter term is on (RoleKV,
+        # "What it does": an activated adapter switches on after the role's
+        # header; the positions before it use the base weights only)
+        self.lr_begin = [0] * n_agents
         self.k = [{s: _Rows((n_kv_heads, head_dim)) for s in seqs} for _ in range(n_layers)]
         self.v = [{s: _Rows((n_kv_heads, head_dim)) for s in seqs} for _ in range(n_layers)]
         # lr[l][seq][plane]; an agent's own rows live in its own plane only
@@ -298,6 +302,14 @@ class CacheModel:
             p = self.plane_of(a)
             if self.lr_cov[layer][SHARED][p] < b or self.lr_cov[layer][a][p] < s:
                 raise OracleError("STATE", "low-rank rows do not cover the view")
+
+    def set_lr_begin(self, agent, pos):
+        """Adapter activation offset of one agent: view positions below pos take
+        no low-rank term (RoleKV, "What it does"; "Challenges we ran into":
+        offsets are passed explicitly)."""
+        if not (0 <= agent < self.N) or int(pos) != pos or pos < 0:
+            raise OracleError("ARG", "lr_begin")
+        self.lr_begin[agent] = int(pos)
 
     def view(self, layer, agent):
         """Agent's view at one layer: K, V_base [L][Hkv][d] and its LR rows [L][r]."""

@@ -8,7 +8,7 @@ from __future__ import annotations
 import numpy as np
 
 from synth import (AppendAgents, AppendBase, AppendLowrank, Attend, Crop, DecodeStep, Schedule,
-                   bf16_bits_to_f64)
+                   SetLrBegin, bf16_bits_to_f64)
 
 from .attention import attention_outputs
 from .cache import CacheModel, OracleError, SHARED
@@ -64,6 +64,8 @@ def apply_event(cache: CacheModel, ev, sample_rows=None):
         cache.append_agents(ev.layer, ev.agents, ev.counts, f(ev.k), f(ev.v), x, a)
     elif isinstance(ev, Crop):
         cache.crop(ev.seq, ev.new_len)
+    elif isinstance(ev, SetLrBegin):
+        cache.set_lr_begin(ev.agent, ev.pos)
     elif isinstance(ev, DecodeStep):
         x = None if ev.x is None else f(ev.x)
         a = None if ev.a is None else f(ev.a)

@@ -161,6 +161,13 @@ class Attend:
 
 
 @dataclass
+class SetLrBegin:
+    """Adapter activation offset of one agent (view position)."""
+    agent: int
+    pos: int
+
+
+@dataclass
 class DecodeStep:
     """One decode token per listed agent: append its row, then attend from it.
     base_len / suffix_len are the lengths before the step."""
@@ -312,6 +319,9 @@ class Schedule:
         for a in agents:
             self.S[layer][a] += 1
         return ev
+
+    def set_lr_begin(self, agent: int, pos: int):
+        self.events.append(SetLrBegin(agent, pos))
 
     def attend(self, kind: str, layer: int, agents: Sequence[int], n_q: Sequence[int], tag=""):
         q = self._q(int(sum(n_q)))

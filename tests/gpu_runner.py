@@ -13,6 +13,7 @@ import torch
 
 from lora_shared_kv_amd import skv as B
 from synth import (AppendAgents, AppendBase, AppendLowrank, Attend, Crop, DecodeStep, Schedule,
+                   SetLrBegin,
                    bf16_bits_to_f64)
 from oracle.run import apply_event, model_for
 
@@ -85,6 +86,8 @@ class GpuRun:
                                 dev(ev.a))
         elif isinstance(ev, Crop):
             B.skv_crop(c, ev.seq, ev.new_len)
+        elif isinstance(ev, SetLrBegin):
+            B.skv_set_lr_begin(c, ev.agent, ev.pos)
         elif isinstance(ev, DecodeStep):
             q = dev(ev.q)
             o = torch.empty_like(q)

@@ -214,6 +214,62 @@ def test_private_prefix_layout(shape_name):
     assert len(res) == 4
 
 
+@pytest.mark.parametrize("shape_name", ["llama3", "qwen3"])
+def test_activation_offsets(shape_name):
+    """Adapter activation offsets (RoleKV, "What it does": the adapter switches
+    on after the role's header): 0, inside the shared prefix, inside the own
+    suffix and beyond the view, through prefill, fused decode steps and a plain
+    decode; the last agent's new tokens lie before its offset."""
+    R = _runner()
+    shape = synth.WORKLOADS[shape_name]
+    N = shape.n_agents
+    prefix, own = 4096, 256
+    sc = synth.Schedule(shape, 1012, n_layers=1)
+    sc.draw_adapters()
+    sc.shared_prefix(prefix)
+    agents = list(range(N))
+    for a in agents:
+        sc.attach(a)
+    offsets = [0, 1000, prefix + 37, 1 << 20][:N] if N > 2 else [1000, prefix + 37]
+    for a, t in zip(agents, offsets):
+        sc.set_lr_begin(a, t)
+    sc.own_rows(0, agents, [own] * N)
+    sc.attend("prefill", 0, agents, [64] * N, tag="offsets prefill")
+    for t in range(3):
+        sc.decode_step(0, agents, tag=f"offsets step {t}")
+    sc.own_rows(0, agents, [1] * N)
+    sc.attend("decode", 0, agents, [1] * N, tag="offsets decode")
+    _, _, res = R.run_parity(sc, log=log)
+    assert len(res) == 5
+
+
+@pytest.mark.parametrize("shape_name", ["llama3", "qwen3"])
+def test_activation_offset_boundaries(shape_name):
+    """V_base = 0, so the output is the adapter term alone, and each agent's
+    offset sits a few keys before the end of its view: a key masked or kept
+    by mistake changes the output by 10-100%, well past the tolerance."""
+    R = _runner()
+    shape = synth.WORKLOADS[shape_name]
+    N = shape.n_agents
+    prefix, own = 2048, 64
+    sc = synth.Schedule(shape, 1013, n_layers=1, zero_vbase=True)
+    sc.draw_adapters()
+    sc.shared_prefix(prefix)
+    agents = list(range(N))
+    for a in agents:
+        sc.attach(a)
+    sc.own_rows(0, agents, [own] * N)
+    L = prefix + own
+    for a, back in zip(agents, [1, 2, 5, 9]):
+        sc.set_lr_begin(a, L - back)
+    sc.attend("prefill", 0, agents, [16] * N, tag="boundary prefill")
+    sc.attend("decode", 0, agents, [1] * N, tag="boundary decode")
+    for t in range(2):
+        sc.decode_step(0, agents, tag=f"boundary step {t}")
+    _, _, res = R.run_parity(sc, log=log)
+    assert len(res) == 4
+
+
 def test_lr_only_term():
     """V_base = 0: the output is only (P V_lr) B_i, about 10x smaller than usual."""
     R = _runner()

@@ -411,6 +411,71 @@ def test_private_copies_equal_shared_prefix(mode):
     assert np.allclose(o_sh, o_pv, rtol=RTOL, atol=RTOL)
 
 
+def _offset_caches(mode, t, seed=43):
+    """Two caches over the same base rows: in the first every position has its
+    low-rank row X A; in the second the positions below t have zero rows
+    (adapter off), the rest the same rows. Returns (with_rows, zero_rows, B, q)."""
+    rng = np.random.default_rng(seed)
+    hq, hkv, d, r, N, hidden, P, own = 4, 2, 64, 4, 2, 64, 7, 5
+    planes = N if mode == BASE_SHARED else 1
+    A = rng.standard_normal((planes, hidden, r)) / math.sqrt(hidden)
+    B = rng.standard_normal((N, r, hkv * d)) * 0.5
+    k, v = rng.standard_normal((P, hkv, d)), rng.standard_normal((P, hkv, d))
+    x = rng.standard_normal((P, hidden))
+    ko, vo = rng.standard_normal((N, own, hkv, d)), rng.standard_normal((N, own, hkv, d))
+    xo = rng.standard_normal((N, own, hidden))
+    caches = []
+    for zero_before in (False, True):
+        c = CacheModel(1, hq, hkv, d, hidden, r, N, mode, 4, 256)
+        c.append_base(0, SHARED, k, v)
+        for p_ in range(planes):
+            if zero_before and t > 0:
+                c.append_lowrank(0, SHARED, p_, min(t, P), None, None)
+                if t < P:
+                    c.append_lowrank(0, SHARED, p_, P - t, x[t:], A[p_])
+            else:
+                c.append_lowrank(0, SHARED, p_, P, x, A[p_])
+        for a in range(N):
+            pl = c.plane_of(a)
+            c.crop(a, P)
+            c.append_base(0, a, ko[a], vo[a])
+            cut = min(max(t - P, 0), own) if zero_before else 0
+            if cut:
+                c.append_lowrank(0, a, pl, cut, None, None)
+            if own - cut:
+                c.append_lowrank(0, a, pl, own - cut, xo[a][cut:], A[pl])
+        caches.append(c)
+    q = rng.standard_normal((N * 3, hq, d))
+    return caches[0], caches[1], B, q
+
+
+@pytest.mark.parametrize("mode", [BASE_SHARED, BASE_LR_SHARED])
+@pytest.mark.parametrize("t", [0, 3, 7, 9, 12, 40])
+def test_activation_offset_equals_zero_rows(mode, t):
+    """An adapter activation offset t (RoleKV, "What it does": the adapter is
+    on only after the role's header) gives the outputs of a cache whose rows
+    below t were appended with the adapter off (zero low-rank rows)."""
+    with_rows, zero_rows, B, q = _offset_caches(mode, t)
+    for a in range(with_rows.N):
+        with_rows.set_lr_begin(a, t)
+    ag = list(range(with_rows.N))
+    o1 = oracle.attention_outputs(with_rows, 0, ag, [3] * len(ag), q, B)
+    o0 = oracle.attention_outputs(zero_rows, 0, ag, [3] * len(ag), q, B)
+    assert np.allclose(o1, o0, rtol=RTOL, atol=RTOL)
+    if t == 0:  # no offset: the rows are on everywhere
+        assert np.array_equal(with_rows.lr_begin, [0, 0])
+    if t >= 12:  # offset past every view: plain base attention (B = 0)
+        ob = oracle.attention_outputs(with_rows, 0, ag, [3] * len(ag), q, np.zeros_like(B))
+        assert np.allclose(o1, ob, rtol=RTOL, atol=RTOL)
+
+
+def test_activation_offset_rejects_bad_arguments():
+    c, A, B = _small_cache()
+    for agent, pos in ((-1, 0), (2, 0), (0, -1)):
+        with pytest.raises(OracleError):
+            c.set_lr_begin(agent, pos)
+
+
 def test_errors_leave_state_unchanged():
     c = CacheModel(1, 4, 2, 64, 64, 4, 2, BASE_SHARED, 4, 3)
     k = np.zeros((9, 2, 64))
