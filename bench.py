@@ -37,11 +37,29 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
 WORKLOADS = {
-    # name: (layers, Hq, Hkv, d, hidden, r, agents, mode, prefix)
+    # name: (layers, Hq, Hkv, d, hidden, r, agents, mode (1 BaseLRShared, 0 BaseShared), prefix)
     "llama3-8b-attn-32k": (32, 32, 8, 128, 4096, 8, 4, 1, 32768),
     "llama3-8b-attn-33k": (32, 32, 8, 128, 4096, 8, 4, 1, 33792),
     "llama3-8b-attn-66k": (32, 32, 8, 128, 4096, 8, 4, 1, 67584),
+    # the other workloads' shapes (their decode and prefill legs, and the many-agent mixed step)
+    "tiny-1l-d64-1k": (1, 14, 2, 64, 896, 8, 2, 0, 1024),
+    "qwen2.5-1.5b-attn-1k": (28, 12, 2, 128, 1536, 16, 2, 0, 1024),
+    "qwen2.5-1.5b-attn-2k": (28, 12, 2, 128, 1536, 16, 2, 0, 2048),
+    "qwen2.5-1.5b-attn-4k": (28, 12, 2, 128, 1536, 16, 2, 0, 4096),
+    "qwen2.5-1.5b-attn-8k": (28, 12, 2, 128, 1536, 16, 2, 0, 8192),
+    "qwen3-1.7b-attn-8k": (28, 16, 8, 128, 2048, 16, 2, 0, 8192),
+    "many-agent-28l-16k": (28, 16, 8, 128, 2048, 16, 8, 0, 16384),
 }
+
+
+def split_kernel_name(d, rows, planes, r):
+    """Template arguments the library picks for the split pass (row blocks of 16
+    stacked query rows, low-rank blocks of 16 stacked plane ranks)."""
+    rb = (rows + 15) // 16
+    rb = 1 if rb <= 1 else (2 if rb <= 2 else 4)
+    mb = (planes * r + 15) // 16
+    mb = 1 if mb <= 1 else (2 if mb <= 2 else (4 if mb <= 4 else 8))
+    return f"decode_split_kernel<{d},{rb},{mb}>"
 
 
 def decode_split_bytes(Hkv, d, r, hidden, prefix, suffixes, n_agents, Hq, bls=True):
@@ -145,6 +163,9 @@ def main():
                     help="adapter mode instead of the workload's (BaseShared: one A_i per agent)")
     ap.add_argument("--ttft", action="store_true",
                     help="also time one new agent's first token: its rows and prefill on every layer")
+    ap.add_argument("--mixed", type=int, default=0, metavar="K",
+                    help="also time K mixed steps: the first half of the agents append and prefill 512 "
+                         "own tokens while the second half decode one token, on every layer")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
     args = ap.parse_args()
@@ -165,7 +186,7 @@ def main():
     G = Hq // Hkv
     total_steps = args.warmup + args.steps
     prefill_n = 512
-    own_max = args.warmup + 2 * args.steps + (0 if args.no_prefill else prefill_n)
+    own_max = args.warmup + 2 * args.steps + (0 if args.no_prefill else prefill_n) + args.mixed * (prefill_n + 1)
     if private:
         max_pages = N * ((prefix + own_max) // 64 + 2) + 4
     else:
@@ -293,7 +314,7 @@ def main():
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                     "measured_peak": round(stream_gbs, 1),
                     "frac_of_measured": round(achieved / stream_gbs, 4),
-                    "kernel": "decode_split_kernel<128,1,1>",
+                    "kernel": split_kernel_name(d, N * G, N if mode == 0 else 1, r),
                     "algorithmic_bytes_per_launch": int(bytes_avg),
                     "avg_launch_us": round(avg_split_s * 1e6, 3)}
     per_kernel = {k: {"ms_total": round(v[0], 3), "launches": v[1],
@@ -320,12 +341,40 @@ def main():
         fl = prefill_flops(Hq, d, r, [base0 + Ssuf] * N, [prefill_n] * N)
         tf = fl / (pms / 1e3 / pn) / 1e12
         prefill = {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                   "frac": round(tf / BF16_PEAK_TFLOPS, 4), "kernel": "prefill_kernel<128,1,2,8>",
+                   "frac": round(tf / BF16_PEAK_TFLOPS, 4), "kernel": f"prefill_kernel<{d},{(r + 15) // 16},2,8,false>",
                    "measured_peak": round(mfma_tflops, 1), "frac_of_measured": round(tf / mfma_tflops, 4),
                    "flops_per_launch": fl, "avg_launch_ms": round(pms / pn, 4),
                    "ms_all_layers": round(pms, 3), "n_q_per_agent": prefill_n,
                    "view": base0 + Ssuf}
         S = [Ssuf] * N
+
+    # ---- mixed steps (the many-agent turn): half the agents prefill 512 own
+    # tokens while the other half decode one token each, on every layer ----
+    mixed = None
+    if args.mixed and N >= 2 and not args.no_prefill:
+        grp_p, grp_d = agents[:N // 2], agents[N // 2:]
+        np_ = len(grp_p)
+        kx, vx, xx = randn(np_ * prefill_n, Hkv, d), randn(np_ * prefill_n, Hkv, d), randn(np_ * prefill_n, hidden)
+        qx = randn(np_ * prefill_n, Hq, d)
+        ox = torch.empty_like(qx)
+        nd = len(grp_d)
+        kd, vd, xd, qd = randn(nd, Hkv, d), randn(nd, Hkv, d), randn(nd, hidden), randn(nd, Hq, d)
+        od = torch.empty_like(qd)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.mixed):
+            for l in range(L):
+                B.skv_append_agents(ctx, l, grp_p, [prefill_n] * np_, kx, vx, xx, A)
+                B.skv_attn_prefill(ctx, l, grp_p, [base0] * np_, [S[a] + prefill_n for a in grp_p],
+                                   [prefill_n] * np_, qx, Bw, ox)
+                B.skv_decode_step(ctx, l, grp_d, [base0] * nd, [S[a] for a in grp_d], kd, vd, xd, A, qd, Bw, od)
+            for a in grp_p:
+                S[a] += prefill_n
+            for a in grp_d:
+                S[a] += 1
+        torch.cuda.synchronize()
+        mixed = {"ms_per_step": round(1e3 * (time.perf_counter() - t0) / args.mixed, 3), "steps": args.mixed,
+                 "prefill_agents": np_, "prefill_tokens": prefill_n, "decode_agents": nd}
 
     # ---- time to first token of one new agent (agent 0 starts over): its rows
     # and its prefill on every layer, then one decode step. Shared layout: its
@@ -381,6 +430,8 @@ def main():
     }
     if ttft is not None:
         res["ttft"] = ttft
+    if mixed is not None:
+        res["mixed"] = mixed
     if not args.no_cpu_baseline and default_run:
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
     print(json.dumps(res), flush=True)
