@@ -338,6 +338,7 @@ def main():
         pt = B.skv_collect_timing(ctx)
         B.skv_set_timing(ctx, False)
         pms, pn = pt["prefill"]
+        pn = L  # one call per layer; a call whose key ranges are split also launches a merge
         fl = prefill_flops(Hq, d, r, [base0 + Ssuf] * N, [prefill_n] * N)
         tf = fl / (pms / 1e3 / pn) / 1e12
         prefill = {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -948,6 +948,11 @@ struct PrefillParams {
   int ag_lrb[SKV_MAX_AGENTS];    // adapter activation offset (view position)
   int blk0[SKV_MAX_AGENTS + 1];  // prefix sums of query blocks per agent
   float scale_log2;
+  // key-range split: workgroup w takes block w % nblk and the range w / nblk
+  // of its pages; with ksplit > 1 it writes partial rows (W floats: o, o_lr,
+  // m, l) to part for the merge instead of the output
+  int ksplit, nblk, W;
+  float* part;
 };
 
 // LDS image of one page of one KV head: the K tile and the V^T tile (64 x D
@@ -988,8 +993,10 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
   extern __shared__ __attribute__((aligned(16))) u16 s_kv[];  // [3][PE]
   __shared__ int32_t s_pages[kMaxViewPages];
   __shared__ float s_lr[NW][16][33];
-  const int g = blockIdx.x % p.Hkv;
-  int qb = blockIdx.x / p.Hkv;
+  const int split = blockIdx.x / p.nblk;
+  const int bid = blockIdx.x % p.nblk;  // blocks of one KV head share blockIdx mod Hkv (and an XCD)
+  const int g = bid % p.Hkv;
+  int qb = bid / p.Hkv;
   int ai = 0;
   while (qb >= p.blk0[ai + 1]) ++ai;
   qb -= p.blk0[ai];
@@ -1007,10 +1014,15 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
   const int np_sh = (min(b, t_max + 1) + kPage - 1) / kPage;
   const int own_keys = max(0, min(S, t_max + 1 - b));
   const int np_own = (own_keys + kPage - 1) / kPage;
-  const int n_pages = np_sh + np_own;
+  // this workgroup's pages [p_lo, p_hi) of the block's view; below, page
+  // indices are local to the range (p_lo + i is the view's page)
+  const int p_lo = (int)((int64_t)split * (np_sh + np_own) / p.ksplit);
+  const int p_hi = (int)((int64_t)(split + 1) * (np_sh + np_own) / p.ksplit);
+  const int n_pages = p_hi - p_lo;
   const int32_t* tsh = p.tbl;
   const int32_t* tow = p.tbl + (1 + p.ag_id[ai]) * p.tbl_seq;
-  for (int i = threadIdx.x; i < n_pages; i += blockDim.x) s_pages[i] = i < np_sh ? tsh[i] : tow[i - np_sh];
+  for (int i = threadIdx.x; i < n_pages; i += blockDim.x)
+    s_pages[i] = p_lo + i < np_sh ? tsh[p_lo + i] : tow[p_lo + i - np_sh];
 
   bf16x8 qf[RB][KS];
   int tpos[RB];
@@ -1059,7 +1071,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
   // lr_keep(i, h): mask of the lane's eight keys of page i, half h.
   const int lr_on_at = p.ag_lrb[ai];
   auto lr_keep = [&](int i, int h) -> u32x4 {
-    const int pstart = i >= np_sh ? b + (i - np_sh) * kPage : i * kPage;  // view position of the page
+    const int ia = p_lo + i;
+    const int pstart = ia >= np_sh ? b + (ia - np_sh) * kPage : ia * kPage;  // view position of the page
     const int nm = lr_on_at - (pstart + 32 * h + 8 * q);
     u32x4 m;
 #pragma unroll
@@ -1282,8 +1295,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
   constexpr float kSlack = 8.f;
   auto softmax_phase = [&](int i) {
     const u16* kvi = s_kv + (i % 3) * PE + 64 * D;  // V^T tile of page i
-    const bool own = i >= np_sh;
-    const int pg_key0 = (own ? i - np_sh : i) * kPage;  // first key of the page in its segment
+    const int ia = p_lo + i;                         // the view's page
+    const bool own = ia >= np_sh;
+    const int pg_key0 = (own ? ia - np_sh : ia) * kPage;  // first key of the page in its segment
     const int vbase = own ? b : 0;                       // view position of segment key 0
     const int seg_lim = own ? S : b;                     // keys beyond the segment are invalid
     // every row of the wave sees all 64 keys of the page
@@ -1399,6 +1413,33 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
   }
   __syncthreads();
 
+  if (p.ksplit > 1) {
+    // partial state of this key range for the merge: o and o_lr unnormalised,
+    // the reference max m (log2 units) and the denominator l
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float l = ones_row ? __shfl(lacc[rb][0][0], n + 4 * p.r) : xsum16_32(l_run[rb]);
+      const int pr = w * 16 * RB + rb * 16 + n;
+      if (row_blk0 + pr < rows_total) {
+        float* pp = p.part + ((uint64_t)blockIdx.x * ROWS + pr) * p.W;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(pp + db * 16 + 4 * q) = oacc[rb][db];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int k = mb * 16 + 4 * q + jj;
+            if (k < p.r) pp[D + k] = lacc[rb][mb][jj];
+          }
+        if (q == 0) {
+          pp[D + p.r] = m_run[rb];
+          pp[D + p.r + 1] = l;
+        }
+      }
+    }
+    return;
+  }
+
   // finalize: o = (oacc + lacc . B_i) / l, B_i applied once for the block's rows
   const int HD = p.Hkv * D;
   const u16* Bi = p.B + (uint64_t)p.ag_id[ai] * p.r * HD + g * D;
@@ -1443,6 +1484,72 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
     }
     __syncthreads();
   }
+}
+
+// prefill workgroup shape: waves, and 16-row blocks per wave
+constexpr int kPrefNW = 8;
+constexpr int kPrefRB = 2;
+
+// Merge of a split prefill: one wave per query row combines the partial rows
+// of its key ranges (s = 0 .. ksplit - 1 at part[((s nblk + block) 256 + row)
+// W]): M = max m_s, w_s = 2^(m_s - M), o = sum w_s o_s / sum w_s l_s and
+// likewise o_lr; then o += o_lr B_i[:, g D:(g + 1) D] once, in bf16.
+struct PrefillMergeParams {
+  const float* part;
+  const u16* B;
+  u16* o;
+  int Hkv, Hq, G, r, W, ksplit, nblk, n;
+  int ag_id[SKV_MAX_AGENTS], ag_nq[SKV_MAX_AGENTS], ag_row0[SKV_MAX_AGENTS];
+  int blk0[SKV_MAX_AGENTS + 1];
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillMergeParams p) {
+  constexpr int ROWS = kPrefNW * 16 * kPrefRB, EPL = D / 64;  // rows per block, elements per lane
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= p.nblk * ROWS) return;
+  const int bid = row / ROWS, pr = row % ROWS;
+  const int g = bid % p.Hkv;
+  int qb = bid / p.Hkv;
+  int ai = 0;
+  while (qb >= p.blk0[ai + 1]) ++ai;
+  qb -= p.blk0[ai];
+  const int rho = qb * ROWS + pr;
+  if (rho >= p.ag_nq[ai] * p.G) return;  // the whole wave leaves together
+  auto prow = [&](int s) { return p.part + (((uint64_t)s * p.nblk + bid) * ROWS + pr) * p.W; };
+  float m_s = -1e30f, l_s = 0.f;
+  if (lane < p.ksplit) {
+    m_s = prow(lane)[D + p.r];
+    l_s = prow(lane)[D + p.r + 1];
+  }
+  const float M = wave_max(m_s);
+  const float w_s = lane < p.ksplit ? __builtin_amdgcn_exp2f(m_s - M) : 0.f;
+  const float L = wave_sum(w_s * l_s);
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float acc[EPL], acc_lr = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int s = 0; s < p.ksplit; ++s) {
+    const float ws = __shfl(w_s, s);
+    const float* pp = prow(s);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += ws * pp[lane + 64 * e];
+    if (lane < p.r) acc_lr += ws * pp[D + lane];
+  }
+  const int HD = p.Hkv * D;
+  const u16* Bi = p.B + (uint64_t)p.ag_id[ai] * p.r * HD + g * D;
+  float out[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) out[e] = acc[e] * inv;
+  for (int k = 0; k < p.r; ++k) {
+    const float lk = __shfl(acc_lr, k) * inv;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) out[e] += lk * bf2f(Bi[(uint64_t)k * HD + lane + 64 * e]);
+  }
+  u16* op = p.o + ((uint64_t)(p.ag_row0[ai] + rho / p.G) * p.Hq + g * p.G + rho % p.G) * D;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) op[lane + 64 * e] = f2bf(out[e]);
 }
 
 // ---------------------------------------------------------------------------
@@ -1563,8 +1670,6 @@ int launch_split_t(const skv::Geometry& g, const DecodeParams& p, int items) {
 
 // Prefill workgroups: eight waves of two 16-row blocks each (two waves per
 // SIMD, accumulators in VGPRs), 256 query rows per workgroup.
-constexpr int kPrefNW = 8;
-constexpr int kPrefRB = 2;
 constexpr int prefill_rows(int) { return kPrefNW * 16 * kPrefRB; }
 
 template <int D, int MB, bool LRO>
@@ -1586,6 +1691,19 @@ int launch_prefill(const skv::Geometry& g, const PrefillParams& p, int blocks) {
 template <int D, int MB>
 int launch_prefill_o(const skv::Geometry& g, const PrefillParams& p, int blocks, bool lro) {
   return lro ? launch_prefill<D, MB, true>(g, p, blocks) : launch_prefill<D, MB, false>(g, p, blocks);
+}
+
+// Prefill of few row blocks: each block's key range is split over ksplit
+// workgroups so that the launch fills the CUs; a merge launch combines the
+// partial rows and applies B_i. The partials use the decode scratch (the two
+// kinds of call are ordered on the stream).
+constexpr int kMaxPrefillSplit = 8;
+constexpr int kMinSplitPages = 4;  // pages per workgroup below which a split does not pay
+
+int prefill_split(int nblk, int min_view_pages) {
+  int ks = 1;
+  while (ks < kMaxPrefillSplit && 2 * ks * nblk <= kCUs && min_view_pages >= 2 * ks * kMinSplitPages) ks *= 2;
+  return ks;
 }
 
 template <int D>
@@ -1891,13 +2009,48 @@ int dev_attn_prefill(const Geometry& g, const AttnJob& job) {
     p.blk0[i + 1] = p.blk0[i] + (a.n_q * g.G + rows - 1) / rows;
   }
   p.scale_log2 = 1.4426950408889634f / sqrtf((float)g.D);
-  const int blocks = p.blk0[job.n] * g.Hkv;
-  if (blocks == 0) return SKV_OK;
+  const int nblk = p.blk0[job.n] * g.Hkv;
+  if (nblk == 0) return SKV_OK;
+  int min_view_pages = 1 << 30;
+  for (int i = 0; i < job.n; ++i)
+    min_view_pages = std::min(min_view_pages, (job.ag[i].b + job.ag[i].S + kPage - 1) / kPage);
+  const int ks = prefill_split(nblk, min_view_pages);
+  static_assert((uint64_t)kCUs * prefill_rows(1) <= (uint64_t)kMaxItems * kMaxDecodeRows,
+                "split prefill partials fit the decode scratch");
+  p.ksplit = ks;
+  p.nblk = nblk;
+  p.W = w_of(g);
+  p.part = (float*)(g.arena + g.scratch_off);
   bool lro = false;  // some agent's adapter activation offset lies inside its view
   for (int i = 0; i < job.n; ++i) lro |= job.ag[i].lr_begin > 0;
+  const int blocks = nblk * ks;
+  int rc;
   if (g.D == 128)
-    return mb == 1 ? launch_prefill_o<128, 1>(g, p, blocks, lro) : launch_prefill_o<128, 2>(g, p, blocks, lro);
-  return mb == 1 ? launch_prefill_o<64, 1>(g, p, blocks, lro) : launch_prefill_o<64, 2>(g, p, blocks, lro);
+    rc = mb == 1 ? launch_prefill_o<128, 1>(g, p, blocks, lro) : launch_prefill_o<128, 2>(g, p, blocks, lro);
+  else
+    rc = mb == 1 ? launch_prefill_o<64, 1>(g, p, blocks, lro) : launch_prefill_o<64, 2>(g, p, blocks, lro);
+  if (rc != SKV_OK || ks == 1) return rc;
+  PrefillMergeParams mp{};
+  mp.part = p.part;
+  mp.B = job.B;
+  mp.o = job.o;
+  mp.Hkv = g.Hkv;
+  mp.Hq = g.Hq;
+  mp.G = g.G;
+  mp.r = g.r;
+  mp.W = p.W;
+  mp.ksplit = ks;
+  mp.nblk = nblk;
+  mp.n = job.n;
+  for (int i = 0; i <= job.n; ++i) mp.blk0[i] = p.blk0[i];
+  for (int i = 0; i < job.n; ++i) {
+    mp.ag_id[i] = p.ag_id[i];
+    mp.ag_nq[i] = p.ag_nq[i];
+    mp.ag_row0[i] = p.ag_row0[i];
+  }
+  const dim3 grid((nblk * rows + 3) / 4);
+  return g.D == 128 ? launch(g, 4, prefill_merge_kernel<128>, grid, 0, mp, "prefill_merge_kernel")
+                    : launch(g, 4, prefill_merge_kernel<64>, grid, 0, mp, "prefill_merge_kernel");
 }
 
 int dev_sync(const Geometry& g) {
