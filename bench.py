@@ -140,9 +140,24 @@ def cpu_baseline(cfg, budget_s=15.0):
             break
     per_layer = el / steps
     tok_s = N / (per_layer * L)
+    # the same oracle on a sample of one suffix prefill call (512 own tokens per
+    # agent): a few query rows of each agent, scaled to the call's rows
+    n_pre = 512
+    kx = rng.standard_normal((N * n_pre, Hkv, d))
+    c.append_agents(0, list(range(N)), [n_pre] * N, kx, kx, rng.standard_normal((N * n_pre, hidden)), A)
+    qp = rng.standard_normal((N * n_pre, Hq, d))
+    sample = [a * n_pre + i for a in range(N) for i in (0, n_pre // 2, n_pre - 1)]
+    t1 = time.perf_counter()
+    attention_outputs(c, 0, list(range(N)), [n_pre] * N, qp, Bm, rows=sample)
+    call_s = (time.perf_counter() - t1) / len(sample) * N * n_pre
+    view = prefix + steps + n_pre
+    flops = prefill_flops(Hq, d, r, [view] * N, [n_pre] * N)
     return {"value": round(tok_s, 4), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{steps} decode steps of 1 layer (4 agents, fp64, prefix {prefix}) timed for "
-                      f"{el:.1f} s; per-layer time x {L} layers"}
+                      f"{el:.1f} s; per-layer time x {L} layers",
+            "prefill": {"value": round(flops / call_s / 1e12, 6), "unit": "TFLOP/s",
+                        "sample": f"{len(sample)} of the {N * n_pre} query rows of one prefill call "
+                                  f"(4 agents x {n_pre} tokens, view {view}), time scaled to all rows"}}
 
 
 def main():
