@@ -74,6 +74,79 @@ def decode_split_bytes(Hkv, d, r, hidden, prefix, suffixes, n_agents, Hq, bls=Tr
     return shared + own + 2 * n_agents * Hq * d + append
 
 
+def project_flops(Hq, Hkv, d, hidden, r, rows):
+    """Algorithmic flops of one front-end call: x [rows][hidden] times the
+    stacked q, k, v weights and the rank-r A."""
+    return 2 * rows * hidden * ((Hq + 2 * Hkv) * d + r)
+
+
+def project_bytes(Hq, Hkv, d, hidden, r, rows, planes):
+    """Algorithmic bytes of one front-end call: the weights, x and A read once;
+    q, k, v and the low-rank rows written once."""
+    return 2 * ((Hq + 2 * Hkv) * d * hidden + rows * hidden + planes * hidden * r
+                + rows * (Hq + 2 * Hkv) * d + rows * r)
+
+
+def frontend_timing(B, cfg, randn, reps=20):
+    """Times skv_project_append on one layer (HIP events on the library's
+    stream): one row per agent (the decode step's shape, bound by streaming the
+    weights) and 512 rows of one agent (a suffix, bound by the matrix cores).
+    For context, the same products as one hipBLASLt GEMM (torch.matmul, no
+    rotation, no writes into pages)."""
+    import torch
+    Hq, Hkv, d, hidden, r, N, mode = (cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["hidden"],
+                                      cfg["rank"], cfg["n_agents"], cfg["mode"])
+    F = (Hq + 2 * Hkv) * d
+    cfg = dict(cfg, max_pages=64)  # rows are cropped after every call
+    arena = torch.zeros(B.skv_arena_bytes(cfg), dtype=torch.uint8, device="cuda")
+    ctx = B.skv_create(cfg, arena)
+    w = randn(F, hidden, var=1.0 / hidden)
+    wp = torch.empty_like(w)
+    B.skv_pack_qkv(ctx, w, wp)
+    A = randn(*((N, hidden, r) if mode == 0 else (hidden, r)), var=1.0 / hidden)
+    out = {}
+    for name, agents, counts in (("decode_rows", list(range(N)), [1] * N), ("suffix_rows", [0], [512])):
+        T = sum(counts)
+        x = randn(T, hidden)
+        q = torch.empty(T, Hq, d, dtype=torch.bfloat16, device="cuda")
+        for _ in range(3):
+            B.skv_project_append(ctx, 0, agents, counts, x, wp, A, 500000.0, q)
+            for a in agents:
+                B.skv_crop(ctx, a, 0)
+        B.skv_set_timing(ctx, True, ["project"])
+        B.skv_collect_timing(ctx)
+        for _ in range(reps):
+            B.skv_project_append(ctx, 0, agents, counts, x, wp, A, 500000.0, q)
+            for a in agents:
+                B.skv_crop(ctx, a, 0)
+        ms, n = B.skv_collect_timing(ctx)["project"]
+        B.skv_set_timing(ctx, False)
+        us = 1e3 * ms / n
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(3):
+            x @ w.t()
+        e0.record()
+        for _ in range(reps):
+            x @ w.t()
+        e1.record()
+        torch.cuda.synchronize()
+        gemm_us = 1e3 * e0.elapsed_time(e1) / reps
+        fl = project_flops(Hq, Hkv, d, hidden, r, T)
+        by = project_bytes(Hq, Hkv, d, hidden, r, T, N if mode == 0 else 1)
+        rec = {"rows": T, "avg_launch_us": round(us, 3), "flops": fl, "bytes": by,
+               "tflops": round(fl / us / 1e6, 1), "gbs": round(by / us / 1e3, 1),
+               "kernel": f"project_kernel<{d},{16 if T <= 16 else 64},{'true' if T <= 16 else 'false'}>",
+               "hipblaslt_gemm_only_us": round(gemm_us, 3)}
+        if T <= 16:
+            rec.update(bound="hbm", peak=HBM_PEAK_GBS, unit="GB/s", frac=round(by / us / 1e3 / HBM_PEAK_GBS, 4))
+        else:
+            rec.update(bound="mfma", peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                       frac=round(fl / us / 1e6 / BF16_PEAK_TFLOPS, 4))
+        out[name] = rec
+    B.skv_destroy(ctx)
+    return out
+
+
 def prefill_flops(Hq, d, r, views, n_q):
     """Algorithmic flops of one prefill call: visible causal pairs only."""
     tot = 0
@@ -181,6 +254,9 @@ def main():
     ap.add_argument("--mixed", type=int, default=0, metavar="K",
                     help="also time K mixed steps: the first half of the agents append and prefill 512 "
                          "own tokens while the second half decode one token, on every layer")
+    ap.add_argument("--frontend", action="store_true",
+                    help="also time the fused front end (skv_project_append) on one layer of the workload: "
+                         "one row per agent (a decode step) and 512 rows of one agent (a suffix)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
     args = ap.parse_args()
@@ -421,6 +497,10 @@ def main():
         ttft = {"ms": round(1e3 * (time.perf_counter() - t0), 3), "rows_appended_per_layer": n_new + 1,
                 "queries_prefilled_per_layer": n_new}
 
+    frontend = None
+    if args.frontend:
+        frontend = frontend_timing(B, dict(c, n_layers=1), randn, reps=20)
+
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -446,6 +526,8 @@ def main():
     }
     if ttft is not None:
         res["ttft"] = ttft
+    if frontend is not None:
+        res["frontend"] = frontend
     if mixed is not None:
         res["mixed"] = mixed
     if not args.no_cpu_baseline and default_run:

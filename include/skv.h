@@ -132,6 +132,43 @@ int skv_append_agents(skv_ctx* ctx, int layer, int n, const int* agents, const i
                       const skv_bf16* k, const skv_bf16* v, const skv_bf16* x,
                       const skv_bf16* A);
 
+/* Front-end weights: reorder the stacked projection weights w_qkv (device
+ * [(Hq + 2 Hkv) d][hidden]; rows = the Hq query heads, then the Hkv key heads,
+ * then the Hkv value heads, d rows each, so that q = x w_q^T etc.) into
+ * w_packed (device, the same size, not overlapping), the layout
+ * skv_project_append streams: for 64-row unit u (head u / (d/64), rows
+ * 32 (u % (d/64)) + [0, 32) and the same + d/2 of that head), 64-column step
+ * s, and m = 0..7, lane l = 0..63, the 8 elements at
+ * ((u * hidden/64 + s) * 8 + m) * 512 + 8 l are
+ *   w_qkv[head d + 32 (u % (d/64)) + 16 (m/2 % 2) + (d/2)(m/4) + l % 16]
+ *        [64 s + 32 (m % 2) + 8 (l / 16) .. + 8],
+ * so each matrix-core operand read is 1 KB of contiguous memory. Done once
+ * per layer when the weights are loaded; enqueued on the context stream.
+ * Errors: ARG. */
+int skv_pack_qkv(skv_ctx* ctx, const skv_bf16* w_qkv, skv_bf16* w_packed);
+
+/* Front end fused with a2 + a3: for each listed agent, project counts[i] new
+ * input rows into q, k and the base v with one GEMM against the base weights,
+ * rotate q and k, and append k, v and the low-rank rows bf16(X A_i) to the
+ * agent's own pages in the same launch (LRAgent review, "What carries the
+ * argument": the base value and the rank-r rows X A_i come from the same X;
+ * the base K/V is computed with the base weights for every agent).
+ *   x: device [sum counts][hidden], agent blocks in call order.
+ *   w_packed: the layer's weights as packed by skv_pack_qkv.
+ *   A: as in skv_append_agents, or NULL for adapter-off zero low-rank rows.
+ *   rope_theta: rotary base, 0 = no rotation. Rotary embedding in the
+ *     rotate-half form: for head vector u and view position t, each pair
+ *     (u[j], u[j + d/2]), j < d/2, turns by the angle t * theta^(-2j/d). The
+ *     view position of own row s of agent i is b_i + s (the shared prefix
+ *     keeps positions 0 .. b_i - 1).
+ *   q_out: device [sum counts][Hq][d], written (bf16, rotated).
+ * q, k and v are rounded once to bf16 from fp32 accumulation. Each agent's
+ * own low-rank rows must be level with its base rows before the call.
+ * Errors: ARG, STATE, OOM (nothing is appended). */
+int skv_project_append(skv_ctx* ctx, int layer, int n, const int* agents, const int* counts,
+                       const skv_bf16* x, const skv_bf16* w_packed, const skv_bf16* A,
+                       float rope_theta, skv_bf16* q_out);
+
 /* a4: suffix prefill attention at one layer. For each listed agent i (host
  * arrays agents/base_len/suffix_len/n_q of length n), the queries are the last
  * n_q[i] positions of its view, already appended. base_len[i] and
@@ -231,8 +268,9 @@ int skv_get_counters(const skv_ctx* ctx, skv_counters* out);
 
 /* Kernel timing with HIP events recorded on the context stream around each
  * launch, while enabled. Kinds: 0 append K/V, 1 append low-rank, 2 decode
- * attention (split pass), 3 decode merge + B, 4 prefill attention. */
-#define SKV_KERNEL_KINDS 5
+ * attention (split pass), 3 decode merge + B, 4 prefill attention, 5 front-end
+ * projection (skv_project_append). */
+#define SKV_KERNEL_KINDS 6
 typedef struct skv_kernel_times {
   double ms[SKV_KERNEL_KINDS];
   int64_t launches[SKV_KERNEL_KINDS];

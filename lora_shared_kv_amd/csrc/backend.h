@@ -70,6 +70,20 @@ struct AttnJob {
   uint16_t* o;        // [sum n_q][Hq][D]
 };
 
+// Front end: the projections of one append job's rows (app: spans with
+// src_row indexing x and q, pages, low-rank rows, table update; app.k and
+// app.v are unused): q, k, v = x W^T, rotary embedding (base theta, 0 = none)
+// on q and k at view position view_off[span] + own row index. q goes to the
+// caller's rows, k and v into the job's pages.
+struct ProjectJob {
+  AppendJob app;
+  const uint16_t* x;  // [rows of the call][hidden]
+  const uint16_t* w;  // packed projection weights (skv_pack_qkv)
+  uint16_t* q;        // [rows of the call][Hq][D]
+  float theta;
+  int32_t view_off[kMaxJobSpans];
+};
+
 // Backend entry points. Each returns an skv_status.
 int dev_check(const Geometry& g);             // SKV_ERR_UNSUPPORTED if the shape is not handled
 uint64_t dev_scratch_bytes(const Geometry& g);  // device scratch the backend needs in the arena
@@ -77,6 +91,8 @@ int dev_init(Geometry& g);
 void dev_fini(Geometry& g);
 int dev_append(const Geometry& g, const AppendJob& job);
 int dev_attn_decode(const Geometry& g, const AttnJob& job);
+int dev_project(const Geometry& g, const ProjectJob& job);
+int dev_pack_qkv(const Geometry& g, const uint16_t* w, uint16_t* out);
 // Fused decode step: job holds lengths before the step; app appends one row
 // per agent (in the same order as job.ag).
 int dev_decode_step(const Geometry& g, const AttnJob& job, const AppendJob& app);

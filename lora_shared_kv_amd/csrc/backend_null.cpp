@@ -17,6 +17,14 @@ int dev_append(const Geometry& g, const AppendJob&) {
   ++*g.launches;
   return SKV_OK;
 }
+int dev_pack_qkv(const Geometry& g, const uint16_t*, uint16_t*) {
+  ++*g.launches;
+  return SKV_OK;
+}
+int dev_project(const Geometry& g, const ProjectJob&) {
+  ++*g.launches;
+  return SKV_OK;
+}
 int dev_attn_decode(const Geometry& g, const AttnJob&) {
   ++*g.launches;
   return SKV_OK;

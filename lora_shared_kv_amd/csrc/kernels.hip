@@ -37,6 +37,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <vector>
@@ -1553,6 +1554,269 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillMergeParams p
 }
 
 // ---------------------------------------------------------------------------
+// Front end: q, k, v projections with rotary embedding, written into pages
+// ---------------------------------------------------------------------------
+
+// The rows X of one append job (some agents' new tokens, consecutive rows of
+// the call) against the stacked projection weights W [(Hq + 2 Hkv) D][hidden]
+// (query heads, then key heads, then value heads): Y^T = W X^T on bf16 MFMA
+// with fp32 accumulation (LRAgent review, "What carries the argument": one pass
+// over X gives q, k and the base value, whose adapter term stays the rank-r
+// rows X A_i). A wave owns 64 output features of one head, d in [32u, 32u + 32)
+// and the same range shifted by D/2, so both members of every rotary pair
+// (d, d + D/2) sit in the same lane of its C tiles, and TM tokens. A workgroup
+// of four waves takes four such units and shares one X tile: X is copied to LDS
+// in MFMA-operand order (each 1 KB fragment is one buffer-to-LDS copy), W goes
+// from memory to registers, both two 64-column stages ahead of the MFMAs. The
+// epilogue rotates q and k, writes q to the caller's rows and k, v into their
+// pages in the K / V^T tile order. Blocks after the GEMM blocks compute the
+// low-rank rows bf16(X A_i) with the append code and write the page tables.
+struct ProjectParams {
+  AppendParams app;  // spans and page ids of the job's rows, low-rank rows, table entries
+  const u16* x;      // [rows of the call][hidden]
+  const u16* w;      // packed weights (pack_qkv_kernel)
+  u16* q;            // [rows of the call][Hq][D]
+  int row0, rows;    // this job's rows of the call: [row0, row0 + rows)
+  int n_units;       // 64-feature units: (Hq + 2 Hkv) D / 64
+  int tok_tiles;     // TM-row tiles of the job
+  int n_gemm;        // GEMM tiles: unit groups of four x token tiles
+  int per_xcd;       // GEMM tiles per XCD; the GEMM part of the grid is 8 per_xcd blocks
+  int Hq, Hkv, hidden;
+  int rope;                           // rotate q and k
+  int view_off[skv::kMaxJobSpans];    // view position of own row 0 of each span's agent (its b_i)
+  double inv_freq[64];                // theta^(-2i/D), i < D/2
+};
+static_assert(sizeof(ProjectParams) <= 4096, "kernel arguments");
+
+// Ring slots of the projection (two stages in flight ahead of the MFMAs;
+// measured: a third slot does not help and slows the split form).
+constexpr int kProjectSlots = 3;
+
+// SK (split K, for few rows): a workgroup takes one unit and one 16-row tile,
+// and its four waves take a quarter of the hidden columns each, with rings of
+// their own; the partial sums meet in LDS at the end. Four times as many
+// workgroups stream W as with four units per workgroup.
+template <int D, int TM, bool SK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void project_kernel(ProjectParams p) {
+  static_assert(!SK || TM == 16, "the split form takes 16-row tiles");
+  constexpr int NC = TM / 16;           // 16-token tiles
+  constexpr int NF = 2 * NC;            // X fragments (16 tokens x 32 columns) per 64-column stage
+  constexpr int NS = kProjectSlots;
+  // u16 per ring slot: X fragments, then 8 W fragments per wave (SK: one wave's ring)
+  constexpr int SLOT = (NF + (SK ? 8 : 32)) * 512;
+  constexpr int RING = (SK ? 4 : 1) * NS * SLOT * 2;
+  static_assert(RING >= 64 * (128 + 8) * 2, "the low-rank blocks stage rows in the same LDS");
+  extern __shared__ __attribute__((aligned(16))) u16 s_pr[];
+  const int b = blockIdx.x;
+  if (b >= 8 * p.per_xcd) {
+    append_block(p.app, b - 8 * p.per_xcd, reinterpret_cast<char*>(s_pr));
+    return;
+  }
+  // Block b runs on XCD b % 8: each XCD takes a contiguous run of tiles, token
+  // tile fastest, so the token tiles of one unit group read W through one L2.
+  const int lb = (b % 8) * p.per_xcd + b / 8;
+  if (lb >= p.n_gemm) return;
+  const int ug = lb / p.tok_tiles, tt = lb % p.tok_tiles;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n = lane & 15, qd = lane >> 4;
+  const int unit = SK ? ug : ug * 4 + wave;
+  const bool active = unit < p.n_units;
+  constexpr int UPH = D / 64;  // units per head
+  const int uc = active ? unit : p.n_units - 1;
+  const int head = uc / UPH, hu = uc % UPH;
+  const int H = p.hidden, nk = H / 64;
+  const int kbeg = SK ? wave * nk / 4 : 0;                // this wave's stages [kbeg, kbeg + kcnt)
+  const int kcnt = SK ? (wave + 1) * nk / 4 - kbeg : nk;
+  u16* const ring = s_pr + (SK ? wave * NS * SLOT : 0);
+  // W is packed (pack_qkv_kernel): the unit's eight fragments of a stage are
+  // 8 KB of contiguous memory, so each copy is 1 KB contiguous and a wave
+  // streams its unit's weights front to back.
+  const __amdgpu_buffer_rsrc_t wr = byte_rsrc(p.w + (uint64_t)uc * nk * 8 * 512, nk * 8 * 1024);
+  // X fragment (c, ks): lane (n, qd) copies token 16 c + n, columns 32 ks + 8 qd + [0, 8).
+  // Rows past the job read as zero (buffer bounds).
+  const __amdgpu_buffer_rsrc_t xr = byte_rsrc(p.x + (uint64_t)p.row0 * H, p.rows * H * 2);
+  const int xoff0 = ((tt * TM + n) * H + 8 * qd) * 2;
+
+  f32x4 acc[NC][4];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[c][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Copies of stage s into ring slot s % NS: this wave's share of the X
+  // fragments, then its own eight W fragments. Stages past the end copy the
+  // last one again, so every stage issues the same copies and the wait below
+  // holds.
+  auto issue = [&](int s) {
+    if (kcnt == 0) return;
+    const int sc = kbeg + (s < kcnt ? s : kcnt - 1);
+    u16* slot = ring + (s % NS) * SLOT;
+    // X fragments per wave: SK all of them; otherwise a quarter (NF < 4:
+    // waves 0 .. NF-1 take one)
+    constexpr int XPW = SK ? NF : (NF >= 4 ? NF / 4 : 1);
+    static_assert(SK || NF < 4 || NF % 4 == 0, "X fragments split evenly over the waves");
+#pragma unroll
+    for (int i = 0; i < XPW; ++i) {
+      const int fi = SK ? i : wave + 4 * i;
+      if (!SK && NF < 4 && fi >= NF) break;
+      const int c = fi >> 1, ks = fi & 1;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (void __attribute__((address_space(3)))*)(slot + fi * 512), 16,
+                                               xoff0 + (16 * c * H + 64 * sc + 32 * ks) * 2, 0, 0, 0);
+    }
+    u16* wdst = slot + (NF + (SK ? 0 : 8 * wave)) * 512;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (void __attribute__((address_space(3)))*)(wdst + (2 * j + ks) * 512),
+                                                 16, ((sc * 8 + 2 * j + ks) * 64 + lane) * 16, 0, 0, 0);
+  };
+  // Before stage s: stages s .. s + NS - 2 are in flight (their X copies, then
+  // 8 W copies each); with no more than NS - 2 stages' worth outstanding, all
+  // of stage s's copies have landed (when the waves' X shares differ, 8 per
+  // stage is the smaller count). The barrier publishes every wave's X copies
+  // and retires the reads of the slot the next issue overwrites.
+  constexpr int kAfter = (NS - 2) * (SK ? NF + 8 : (NF % 4 == 0 ? 8 + NF / 4 : 8));
+  constexpr int kWaitStage = (kAfter & 15) | ((kAfter >> 4) << 14) | (7 << 4) | (15 << 8);
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue(s);
+  for (int s = 0; s < kcnt; ++s) {
+    __builtin_amdgcn_s_waitcnt(kWaitStage);
+    if (!SK) __syncthreads();  // SK: every wave reads only its own ring
+    issue(s + NS - 1);
+    const u16* slot = ring + (s % NS) * SLOT;
+    bf16x8 bx[2][NC], aw[2][4];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        aw[ks][j] = *reinterpret_cast<const bf16x8*>(slot + (NF + (SK ? 0 : 8 * wave) + 2 * j + ks) * 512 + lane * 8);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) bx[ks][c] = *reinterpret_cast<const bf16x8*>(slot + (2 * c + ks) * 512 + lane * 8);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          acc[c][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[ks][j], bx[ks][c], acc[c][j], 0, 0, 0);
+    // every LDS read of the stage first, then the MFMAs (the first ones wait
+    // only for their own operands)
+    __builtin_amdgcn_sched_group_barrier(0x100, 8 + 2 * NC, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8 * NC, 0);
+  }
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): no copy outlives the wave
+  if constexpr (SK) {
+    // waves 1..3 hand their partial sums to wave 0 (added in wave order)
+    __syncthreads();  // every wave is done with its ring
+    float* red = reinterpret_cast<float*>(s_pr);  // [3][64 lanes][16]
+    if (wave > 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4*>(red + ((wave - 1) * 64 + lane) * 16 + 4 * j) = acc[0][j];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[0][j] += *reinterpret_cast<const f32x4*>(red + (w * 64 + lane) * 16 + 4 * j);
+  }
+  if (!active) return;
+
+  const int part = head < p.Hq ? 0 : (head < p.Hq + p.Hkv ? 1 : 2);  // q, k, v
+  const int hh = part == 0 ? head : (part == 1 ? head - p.Hq : head - p.Hq - p.Hkv);
+  constexpr double kTwoPi = 6.283185307179586;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int t = tt * TM + 16 * c + n;
+    if (t >= p.rows) continue;
+    const int row = p.row0 + t;
+    int s = 0;
+    while (s + 1 < p.app.n_spans && row >= p.app.spans[s + 1].src_row) ++s;
+    const skv::Span& sp = p.app.spans[s];
+    const int pos = sp.pos0 + row - sp.src_row;  // own row index
+    const int page = p.app.ids[sp.ids_off + pos / kPage - sp.first_page];
+    const int slot_in_page = pos % kPage;
+    const double view = (double)(p.view_off[s] + pos);
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      const int dlo = 32 * hu + 16 * jp + 4 * qd;  // element 0 of the low half; the high half is + D/2
+      float lo[4], hi[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo[e] = acc[c][jp][e];
+        hi[e] = acc[c][jp + 2][e];
+      }
+      if (part < 2 && p.rope) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // angle in fp64, reduced to [-pi, pi] before the fp32 sine and cosine
+          double a = view * p.inv_freq[dlo + e];
+          a -= rint(a * (1.0 / kTwoPi)) * kTwoPi;
+          float sn, cs;
+          sincosf((float)a, &sn, &cs);
+          const float l = lo[e], h = hi[e];
+          lo[e] = l * cs - h * sn;
+          hi[e] = l * sn + h * cs;
+        }
+      }
+      if (part == 2) {
+        u16* vt = p.app.VT + ((uint64_t)page * p.Hkv + hh) * kPage * D;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vt[v_tile_off<D>(slot_in_page, dlo + e)] = f2bf(lo[e]);
+          vt[v_tile_off<D>(slot_in_page, dlo + D / 2 + e)] = f2bf(hi[e]);
+        }
+      } else {
+        const u32x2 vlo{(uint32_t)f2bf(lo[0]) | ((uint32_t)f2bf(lo[1]) << 16),
+                        (uint32_t)f2bf(lo[2]) | ((uint32_t)f2bf(lo[3]) << 16)};
+        const u32x2 vhi{(uint32_t)f2bf(hi[0]) | ((uint32_t)f2bf(hi[1]) << 16),
+                        (uint32_t)f2bf(hi[2]) | ((uint32_t)f2bf(hi[3]) << 16)};
+        u16 *dl, *dh;
+        if (part == 0) {
+          dl = p.q + ((uint64_t)row * p.Hq + hh) * D + dlo;
+          dh = dl + D / 2;
+        } else {
+          u16* kt = p.app.K + ((uint64_t)page * p.Hkv + hh) * kPage * D;
+          dl = kt + k_tile_off<D>(slot_in_page, dlo);
+          dh = kt + k_tile_off<D>(slot_in_page, dlo + D / 2);
+        }
+        *reinterpret_cast<u32x2*>(dl) = vlo;
+        *reinterpret_cast<u32x2*>(dh) = vhi;
+      }
+    }
+  }
+}
+
+// Packs W [(Hq + 2 Hkv) D][hidden] for project_kernel: for 64-feature unit u
+// (head u / (D / 64), d in [32 hu, 32 hu + 32) and that + D/2), 64-column
+// stage s, fragment f = 2 j + ks and lane l = n + 16 qd, the 16 bytes at
+// ((u * nk + s) * 8 + f) * 1024 + 16 l hold W[row][64 s + 32 ks + 8 qd .. + 8]
+// with row = head D + 32 hu + 16 (j & 1) + (D/2)(j >> 1) + n: the order in which
+// one wave's MFMA A operands are read. One block per (unit, stage).
+struct PackParams {
+  const u16* w;
+  u16* out;
+  int D, H;
+};
+__global__ __launch_bounds__(256) void pack_qkv_kernel(PackParams p) {
+  const u16* __restrict__ w = p.w;
+  u16* __restrict__ out = p.out;
+  const int D = p.D, H = p.H;
+  const int nk = H / 64, uph = D / 64;
+  const int u = blockIdx.x / nk, s = blockIdx.x % nk;
+  const int head = u / uph, hu = u % uph;
+  for (int v = threadIdx.x; v < 512; v += blockDim.x) {
+    const int f = v >> 6, l = v & 63, j = f >> 1, ks = f & 1, n = l & 15, qd = l >> 4;
+    const int row = head * D + 32 * hu + 16 * (j & 1) + (D / 2) * (j >> 1) + n;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(w + (uint64_t)row * H + 64 * s + 32 * ks + 8 * qd);
+    *reinterpret_cast<u32x4*>(out + ((uint64_t)blockIdx.x * 8 + f) * 512 + l * 8) = val;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Measurement probes (roofline calibration; not part of the attention path)
 // ---------------------------------------------------------------------------
 
@@ -1767,6 +2031,69 @@ int dev_append(const Geometry& g, const AppendJob& job) {
   const int blocks = append_blocks(p);
   if (blocks == 0 && !job.update_tables) return SKV_OK;
   return launch(g, job.do_kv ? 0 : 1, append_kernel, dim3(std::max(blocks, 1)), 0, p, "append_kernel");
+}
+
+// The GEMM part takes one 16-token tile in the split form for a few rows (a
+// decode step) and 64-token tiles otherwise (measured: the split form over
+// several row tiles is slower than 64-row tiles already at 64 rows).
+constexpr int kProjectSplitRows = 16;
+template <int D, int TM, bool SK>
+int launch_project_t(const Geometry& g, const ProjectParams& p) {
+  const size_t lds = (size_t)(SK ? 4 : 1) * kProjectSlots * (2 * TM / 16 + (SK ? 8 : 32)) * 512 * sizeof(u16);
+  // the ring exceeds the default dynamic LDS limit (set once per process)
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(project_kernel<D, TM, SK>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) {
+    set_err("hipFuncSetAttribute(project_kernel)", attr);
+    return SKV_ERR_HIP;
+  }
+  const int grid = 8 * p.per_xcd + append_blocks(p.app);
+  return launch(g, 5, project_kernel<D, TM, SK>, dim3(grid), lds, p, "project_kernel");
+}
+
+template <int D>
+int launch_project(const Geometry& g, const ProjectParams& p, int tm) {
+  return tm == 16 ? launch_project_t<D, 16, true>(g, p) : launch_project_t<D, 64, false>(g, p);
+}
+
+int dev_pack_qkv(const Geometry& g, const uint16_t* w, uint16_t* out) {
+  const int units = (g.Hq + 2 * g.Hkv) * g.D / 64;
+  return launch(g, 5, pack_qkv_kernel, dim3(units * (g.hidden / 64)), 0, PackParams{w, out, g.D, g.hidden},
+                "pack_qkv_kernel");
+}
+
+int dev_project(const Geometry& g, const ProjectJob& job) {
+  const AppendJob& a = job.app;
+  if (g.hidden % 64 != 0 || a.n_spans < 1) {
+    set_err("project", hipErrorInvalidValue);
+    return SKV_ERR_UNSUPPORTED;
+  }
+  // k and v come from the GEMM: the append part of the launch writes only the
+  // low-rank rows and the table entries (its K/V copy blocks would read job.k).
+  AppendJob aj = a;
+  aj.do_kv = false;
+  aj.k = aj.v = nullptr;
+  ProjectParams p{};
+  plan_append(g, aj, p.app);
+  p.x = job.x;
+  p.w = job.w;
+  p.q = job.q;
+  p.row0 = a.spans[0].src_row;
+  p.rows = a.spans[a.n_spans - 1].src_row + a.spans[a.n_spans - 1].n - p.row0;
+  p.n_units = (g.Hq + 2 * g.Hkv) * g.D / 64;
+  // up to 16 rows: one unit per workgroup (split K); more rows: four units
+  // and 64 rows per workgroup
+  const int tm = p.rows <= kProjectSplitRows ? 16 : 64;
+  p.tok_tiles = (p.rows + tm - 1) / tm;
+  p.n_gemm = (tm == 16 ? p.n_units : (p.n_units + 3) / 4) * p.tok_tiles;
+  p.per_xcd = (p.n_gemm + 7) / 8;
+  p.Hq = g.Hq;
+  p.Hkv = g.Hkv;
+  p.hidden = g.hidden;
+  p.rope = job.theta != 0.f;
+  for (int s = 0; s < a.n_spans; ++s) p.view_off[s] = job.view_off[s];
+  for (int i = 0; i < g.D / 2; ++i) p.inv_freq[i] = p.rope ? std::pow((double)job.theta, -2.0 * i / g.D) : 0.0;
+  return g.D == 128 ? launch_project<128>(g, p, tm) : launch_project<64>(g, p, tm);
 }
 
 // Decode for the agents of job, in groups that fit one launch. With app (a

@@ -172,6 +172,113 @@ int run_jobs(skv_ctx* c, const std::vector<AppendJob>& jobs) {
   return SKV_OK;
 }
 
+// Checks shared by the calls that append own rows to listed agents: layer,
+// distinct agents, counts, and low-rank rows level with base rows. total gets
+// the row count.
+int check_agent_rows(skv_ctx* c, int layer, int n, const int* agents, const int* counts, long* total) {
+  const Geometry& g = c->g;
+  *total = 0;
+  if (layer < 0 || layer >= g.L) return c->fail(SKV_ERR_ARG, "layer %d out of range", layer);
+  if (n < 0 || n > g.N) return c->fail(SKV_ERR_ARG, "agent count %d", n);
+  if (n == 0) return SKV_OK;
+  if (!agents || !counts) return c->fail(SKV_ERR_ARG, "null agents or counts");
+  uint32_t seen = 0;
+  for (int i = 0; i < n; ++i) {
+    int a = agents[i];
+    if (a >= 0 && a < g.N && (seen >> a & 1u)) return c->fail(SKV_ERR_ARG, "duplicate agent %d", a);
+    if (a >= 0 && a < g.N) seen |= 1u << a;
+  }
+  long tot = 0;
+  for (int i = 0; i < n; ++i) {
+    int a = agents[i];
+    if (a < 0 || a >= g.N || counts[i] < 0)
+      return c->fail(SKV_ERR_ARG, "agent list entry %d (count %d)", a, counts[i]);
+    tot += counts[i];
+  }
+  if (tot == 0) return SKV_OK;
+  const Layer& l = c->layers[layer];
+  for (int i = 0; i < n; ++i) {
+    int slot = 1 + agents[i];
+    if (l.lr_own[agents[i]] != l.len[slot])
+      return c->fail(SKV_ERR_STATE, "agent %d low-rank rows (%d) lag base rows (%d)", agents[i],
+                     l.lr_own[agents[i]], l.len[slot]);
+  }
+  *total = tot;
+  return SKV_OK;
+}
+
+// Pages and jobs of a checked agent-row append. The pages are taken from the
+// free list now; finish_agent_rows commits them or gives them back.
+struct AgentRows {
+  std::vector<std::vector<int32_t>> tables;
+  std::vector<int32_t> taken;
+  std::vector<AppendJob> jobs;
+  int need = 0;
+};
+
+int plan_agent_rows(skv_ctx* c, int layer, int n, const int* agents, const int* counts,
+                    const skv_bf16* k, const skv_bf16* v, const skv_bf16* x, const skv_bf16* A,
+                    AgentRows& ar) {
+  const Geometry& g = c->g;
+  Layer& l = c->layers[layer];
+  for (int i = 0; i < n; ++i) {
+    int slot = 1 + agents[i];
+    ar.need += ceil_div(l.len[slot] + counts[i], g.ps) - (int)l.tbl[slot].size();
+  }
+  if (ar.need > (int)l.free.size())
+    return c->fail(SKV_ERR_OOM, "layer %d: %d pages needed, %d free", layer, ar.need,
+                   (int)l.free.size());
+  ar.tables.resize(n);
+  for (int i = 0; i < n; ++i) {
+    int slot = 1 + agents[i];
+    ar.tables[i] = l.tbl[slot];
+    int want = ceil_div(l.len[slot] + counts[i], g.ps) - (int)ar.tables[i].size();
+    for (int p = 0; p < want; ++p) {
+      int32_t id = *l.free.begin();
+      l.free.erase(l.free.begin());
+      ar.tables[i].push_back(id);
+      ar.taken.push_back(id);
+    }
+  }
+  AppendJob proto{};
+  proto.layer = layer;
+  proto.do_kv = true;
+  proto.do_lr = true;
+  proto.update_tables = true;
+  proto.k = k;
+  proto.v = v;
+  proto.x = x;
+  const uint64_t a_stride = (uint64_t)g.hidden * g.r;
+  int row = 0;
+  for (int i = 0; i < n; ++i) {
+    int a = agents[i];
+    const uint16_t* ap = nullptr;
+    if (x) ap = g.mode == SKV_BASE_SHARED ? A + a_stride * a : A;
+    add_spans(c, ar.jobs, proto, ar.tables[i], 1 + a, l.len[1 + a], counts[i], row, c->plane_of(a), ap);
+    row += counts[i];
+  }
+  return SKV_OK;
+}
+
+int finish_agent_rows(skv_ctx* c, int layer, int n, const int* agents, const int* counts, long total,
+                      bool lr_from_x, AgentRows& ar, int rc) {
+  Layer& l = c->layers[layer];
+  if (rc != SKV_OK) {
+    for (int32_t p : ar.taken) l.free.insert(p);
+    return rc;
+  }
+  for (int i = 0; i < n; ++i) {
+    int slot = 1 + agents[i];
+    l.tbl[slot] = std::move(ar.tables[i]);
+    l.len[slot] += counts[i];
+    l.lr_own[agents[i]] += counts[i];
+  }
+  c->counters.pages_alloc += ar.need;
+  c->counters.base_rows_own += total;
+  (lr_from_x ? c->counters.lr_rows : c->counters.lr_zero_rows) += total;
+  return SKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -298,88 +405,16 @@ int skv_append_agents(skv_ctx* c, int layer, int n, const int* agents, const int
                       const skv_bf16* k, const skv_bf16* v, const skv_bf16* x,
                       const skv_bf16* A) {
   if (!c) return SKV_ERR_ARG;
-  const Geometry& g = c->g;
-  if (layer < 0 || layer >= g.L) return c->fail(SKV_ERR_ARG, "layer %d out of range", layer);
-  if (n < 0 || n > g.N) return c->fail(SKV_ERR_ARG, "agent count %d", n);
-  if (n == 0) return SKV_OK;
-  if (!agents || !counts) return c->fail(SKV_ERR_ARG, "null agents or counts");
   if (x && !A) return c->fail(SKV_ERR_ARG, "x given without A");
-  uint32_t seen = 0;
   long total = 0;
-  for (int i = 0; i < n; ++i) {
-    int a = agents[i];
-    if (a >= 0 && a < g.N && (seen >> a & 1u)) return c->fail(SKV_ERR_ARG, "duplicate agent %d", a);
-    if (a >= 0 && a < g.N) seen |= 1u << a;
-  }
-  for (int i = 0; i < n; ++i) {
-    int a = agents[i];
-    if (a < 0 || a >= g.N || counts[i] < 0)
-      return c->fail(SKV_ERR_ARG, "agent list entry %d (count %d)", a, counts[i]);
-    total += counts[i];
-  }
-  if (total == 0) return SKV_OK;
+  int rc = check_agent_rows(c, layer, n, agents, counts, &total);
+  if (rc != SKV_OK || total == 0) return rc;
   if (!k || !v) return c->fail(SKV_ERR_ARG, "null k or v");
-  Layer& l = c->layers[layer];
-  for (int i = 0; i < n; ++i) {
-    int slot = 1 + agents[i];
-    if (l.lr_own[agents[i]] != l.len[slot])
-      return c->fail(SKV_ERR_STATE, "agent %d low-rank rows (%d) lag base rows (%d)", agents[i],
-                     l.lr_own[agents[i]], l.len[slot]);
-  }
-  int need = 0;
-  for (int i = 0; i < n; ++i) {
-    int slot = 1 + agents[i];
-    need += ceil_div(l.len[slot] + counts[i], g.ps) - (int)l.tbl[slot].size();
-  }
-  if (need > (int)l.free.size())
-    return c->fail(SKV_ERR_OOM, "layer %d: %d pages needed, %d free", layer, need,
-                   (int)l.free.size());
-  std::vector<std::vector<int32_t>> tables(n);
-  std::vector<int32_t> taken;
-  for (int i = 0; i < n; ++i) {
-    int slot = 1 + agents[i];
-    tables[i] = l.tbl[slot];
-    int want = ceil_div(l.len[slot] + counts[i], g.ps) - (int)tables[i].size();
-    for (int p = 0; p < want; ++p) {
-      int32_t id = *l.free.begin();
-      l.free.erase(l.free.begin());
-      tables[i].push_back(id);
-      taken.push_back(id);
-    }
-  }
-  AppendJob proto{};
-  proto.layer = layer;
-  proto.do_kv = true;
-  proto.do_lr = true;
-  proto.update_tables = true;
-  proto.k = k;
-  proto.v = v;
-  proto.x = x;
-  std::vector<AppendJob> jobs;
-  const uint64_t a_stride = (uint64_t)g.hidden * g.r;
-  int row = 0;
-  for (int i = 0; i < n; ++i) {
-    int a = agents[i];
-    const uint16_t* ap = nullptr;
-    if (x) ap = g.mode == SKV_BASE_SHARED ? A + a_stride * a : A;
-    add_spans(c, jobs, proto, tables[i], 1 + a, l.len[1 + a], counts[i], row, c->plane_of(a), ap);
-    row += counts[i];
-  }
-  int rc = run_jobs(c, jobs);
-  if (rc != SKV_OK) {
-    for (int32_t p : taken) l.free.insert(p);
-    return rc;
-  }
-  for (int i = 0; i < n; ++i) {
-    int slot = 1 + agents[i];
-    l.tbl[slot] = std::move(tables[i]);
-    l.len[slot] += counts[i];
-    l.lr_own[agents[i]] += counts[i];
-  }
-  c->counters.pages_alloc += need;
-  c->counters.base_rows_own += total;
-  (x ? c->counters.lr_rows : c->counters.lr_zero_rows) += total;
-  return SKV_OK;
+  AgentRows ar;
+  rc = plan_agent_rows(c, layer, n, agents, counts, k, v, x, A, ar);
+  if (rc != SKV_OK) return rc;
+  rc = run_jobs(c, ar.jobs);
+  return finish_agent_rows(c, layer, n, agents, counts, total, x != nullptr, ar, rc);
 }
 
 static int validate_attend(skv_ctx* c, int layer, int n, const int* agents, const int* base_len,
@@ -541,6 +576,49 @@ int skv_decode_step(skv_ctx* c, int layer, int n, const int* agents, const int* 
   c->counters.base_rows_own += n;
   (x ? c->counters.lr_rows : c->counters.lr_zero_rows) += n;
   return SKV_OK;
+}
+
+int skv_pack_qkv(skv_ctx* c, const skv_bf16* w_qkv, skv_bf16* w_packed) {
+  if (!c) return SKV_ERR_ARG;
+  if (!w_qkv || !w_packed) return c->fail(SKV_ERR_ARG, "null w_qkv or w_packed");
+  const Geometry& g = c->g;
+  const uint64_t bytes = 2ull * (g.Hq + 2 * g.Hkv) * g.D * g.hidden;
+  const uintptr_t a = (uintptr_t)w_qkv, b = (uintptr_t)w_packed;
+  if (a < b + bytes && b < a + bytes) return c->fail(SKV_ERR_ARG, "w_qkv and w_packed overlap");
+  int rc = skv::dev_pack_qkv(g, (const uint16_t*)w_qkv, (uint16_t*)w_packed);
+  if (rc != SKV_OK) return c->fail(rc, "device pack failed: %s", skv::dev_last_error());
+  return SKV_OK;
+}
+
+int skv_project_append(skv_ctx* c, int layer, int n, const int* agents, const int* counts,
+                       const skv_bf16* x, const skv_bf16* w_packed, const skv_bf16* A, float rope_theta,
+                       skv_bf16* q_out) {
+  if (!c) return SKV_ERR_ARG;
+  long total = 0;
+  int rc = check_agent_rows(c, layer, n, agents, counts, &total);
+  if (rc != SKV_OK || total == 0) return rc;
+  if (!x || !w_packed || !q_out) return c->fail(SKV_ERR_ARG, "null x, w_packed or q_out");
+  if (!(rope_theta == 0.f || (rope_theta > 1.f && rope_theta < 1e30f)))
+    return c->fail(SKV_ERR_ARG, "rotary base %g (0 or above 1)", (double)rope_theta);
+  AgentRows ar;
+  rc = plan_agent_rows(c, layer, n, agents, counts, nullptr, nullptr, A ? x : nullptr, A, ar);
+  if (rc != SKV_OK) return rc;
+  for (const AppendJob& j : ar.jobs) {
+    skv::ProjectJob pj{};
+    pj.app = j;
+    pj.app.do_kv = false;  // k and v are written by the projection itself
+    pj.x = (const uint16_t*)x;
+    pj.w = (const uint16_t*)w_packed;
+    pj.q = (uint16_t*)q_out;
+    pj.theta = rope_theta;
+    for (int s = 0; s < j.n_spans; ++s) pj.view_off[s] = c->base_len[j.spans[s].seq_slot - 1];
+    rc = skv::dev_project(c->g, pj);
+    if (rc != SKV_OK) {
+      rc = c->fail(rc, "device projection failed: %s", skv::dev_last_error());
+      break;
+    }
+  }
+  return finish_agent_rows(c, layer, n, agents, counts, total, A != nullptr, ar, rc);
 }
 
 int skv_set_lr_begin(skv_ctx* c, int agent, int pos) {

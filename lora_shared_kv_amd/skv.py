@@ -18,7 +18,7 @@ SKV_SHARED = -1
 SKV_BASE_SHARED = 0
 SKV_BASE_LR_SHARED = 1
 SKV_MAX_AGENTS = 16
-KERNEL_KINDS = ("append_kv", "append_lowrank", "decode_split", "decode_merge", "prefill")
+KERNEL_KINDS = ("append_kv", "append_lowrank", "decode_split", "decode_merge", "prefill", "project")
 
 _CODES = {0: "OK", -1: "ARG", -2: "STATE", -3: "OOM", -4: "UNSUPPORTED", -5: "HIP"}
 
@@ -47,7 +47,7 @@ class skv_counters(ctypes.Structure):
 
 
 class skv_kernel_times(ctypes.Structure):
-    _fields_ = [("ms", ctypes.c_double * 5), ("launches", ctypes.c_int64 * 5)]
+    _fields_ = [("ms", ctypes.c_double * 6), ("launches", ctypes.c_int64 * 6)]
 
 
 EXPORTS = {
@@ -62,6 +62,8 @@ EXPORTS = {
     "skv_decode_step": (_I, [_P, _I, _I, _IP, _IP, _IP, _P, _P, _P, _P, _P, _P, _P]),
     "skv_crop": (_I, [_P, _I, _I]),
     "skv_set_lr_begin": (_I, [_P, _I, _I]),
+    "skv_project_append": (_I, [_P, _I, _I, _IP, _IP, _P, _P, _P, ctypes.c_float, _P]),
+    "skv_pack_qkv": (_I, [_P, _P, _P]),
     "skv_get_lens": (_I, [_P, _I, _IP, _IP, _IP, _IP, _IP]),
     "skv_get_pages": (_I, [_P, _I, _I, ctypes.POINTER(ctypes.c_int32), _I]),
     "skv_get_pools": (_I, [_P, ctypes.POINTER(skv_pools)]),
@@ -228,6 +230,24 @@ def skv_append_agents(ctx: Ctx, layer: int, agents, counts, k, v, x=None, A=None
     ctx._check(ctx.lib.skv_append_agents(
         ctx.handle, layer, n, ag, cn, _ptr(k, shp, "k"), _ptr(v, shp, "v"),
         _ptr(x, (tot, ctx.hidden), "x"), _ptr(A, ctx.a_shape, "A")))
+
+
+def skv_pack_qkv(ctx: Ctx, w_qkv, w_packed):
+    shp = ((ctx.Hq + 2 * ctx.Hkv) * ctx.d, ctx.hidden)
+    ctx._check(ctx.lib.skv_pack_qkv(ctx.handle, _ptr(w_qkv, shp, "w_qkv"), _ptr(w_packed, None, "w_packed")))
+
+
+def skv_project_append(ctx: Ctx, layer: int, agents, counts, x, w_packed, A, rope_theta: float, q_out):
+    """w_packed: the output of skv_pack_qkv (any shape holding (Hq + 2 Hkv) d hidden elements)."""
+    ag, n = _ints(agents)
+    cn, _ = _ints(counts)
+    tot = sum(cn[:n])
+    if w_packed is not None and not isinstance(w_packed, int):
+        if w_packed.numel() != (ctx.Hq + 2 * ctx.Hkv) * ctx.d * ctx.hidden:
+            raise ValueError("w_packed has the wrong number of elements")
+    ctx._check(ctx.lib.skv_project_append(
+        ctx.handle, layer, n, ag, cn, _ptr(x, (tot, ctx.hidden), "x"), _ptr(w_packed, None, "w_packed"),
+        _ptr(A, ctx.a_shape, "A"), float(rope_theta), _ptr(q_out, (tot, ctx.Hq, ctx.d), "q_out")))
 
 
 def skv_attn_prefill(ctx: Ctx, layer: int, agents, base_len, suffix_len, n_q, q, B, o):

@@ -318,36 +318,15 @@ def test_lr_contribution_difference():
 # --------------------------------------------------------------------------
 
 def k_tile_index(D):
-    """Element offset of K[key][c] inside a (page, head) tile (layout in include/skv.h)."""
-    key = np.arange(64)[:, None]
-    c = np.arange(D)[None, :]
-    h, kk = key >> 5, key & 31
-    n, t = 4 * (kk >> 3) + (kk & 3), (kk & 7) >> 2
-    return ((h * 2 + t) * (D // 32) + (c >> 5)) * 512 + (n + 16 * ((c & 31) >> 3)) * 8 + (c & 7)
+    return _runner().k_tile_index(D)
 
 
 def v_tile_index(D):
-    """Element offset of V[key][c] inside a (page, head) tile (layout in include/skv.h)."""
-    key = np.arange(64)[:, None]
-    c = np.arange(D)[None, :]
-    h, kk = key >> 5, key & 31
-    return (h * (D // 16) + (c >> 4)) * 512 + ((c & 15) + 16 * (kk >> 3)) * 8 + (kk & 7)
+    return _runner().v_tile_index(D)
 
 
 def _pool_views(gpu):
-    """Raw pools: K and V as [layer][page][head][64 * d] tiles, LRT as [plane][layer][page][r][64]."""
-    import torch
-    from lora_shared_kv_amd import skv as B
-    c = gpu.cfg
-    p = B.skv_get_pools(gpu.ctx)
-    L, mp, Hkv, d, r = c["n_layers"], c["max_pages"], c["n_kv_heads"], c["head_dim"], c["rank"]
-    a16 = gpu.arena.view(torch.int16)
-    kn = L * mp * Hkv * 64 * d
-    K = a16[p["k_off"] // 2: p["k_off"] // 2 + kn].view(L, mp, Hkv, 64 * d)
-    VT = a16[p["vt_off"] // 2: p["vt_off"] // 2 + kn].view(L, mp, Hkv, 64 * d)
-    ln = p["planes"] * L * mp * r * 64
-    LRT = a16[p["lrt_off"] // 2: p["lrt_off"] // 2 + ln].view(p["planes"], L, mp, r, 64)
-    return K, VT, LRT
+    return _runner().pool_views(gpu)
 
 
 def test_cache_layout_bytes_and_lowrank_rows():

@@ -61,6 +61,8 @@ op = st.one_of(
               st.booleans()),
     st.tuples(st.just("agents"), st.integers(0, 1), st.lists(st.integers(0, 2), min_size=0, max_size=3),
               st.lists(st.integers(0, 5), min_size=3, max_size=3), st.booleans()),
+    st.tuples(st.just("project"), st.integers(0, 1), st.lists(st.integers(0, 2), min_size=0, max_size=3),
+              st.lists(st.integers(0, 5), min_size=3, max_size=3), st.booleans()),
     st.tuples(st.just("crop"), st.integers(-1, 2), st.integers(-1, 16)),
     st.tuples(st.just("attend"), st.integers(0, 1), st.lists(st.integers(0, 2), min_size=1, max_size=3),
               st.integers(0, 2), st.integers(1, 3)),
@@ -115,6 +117,21 @@ def test_random_ops_match_the_oracle(ops, mode):
             try:
                 B.skv_append_agents(ctx, layer, agents, counts, FAKE, FAKE, FAKE if with_x else None,
                                     FAKE if with_x else None); got = "OK"
+            except B.SkvError as e:
+                got = e.code
+        elif kind == "project":
+            # the fused front end appends like skv_append_agents (its k, v come
+            # from the projection; x feeds the low-rank rows when A is given)
+            _, layer, agents, counts, with_a = o
+            counts = counts[:len(agents)]
+            tot = sum(counts)
+            z = np.zeros((tot, Hkv, d))
+            x = np.zeros((tot, hidden)) if with_a else None
+            a = (np.zeros((cfg["n_agents"], hidden, r)) if mode == 0 else np.zeros((hidden, r))) if with_a else None
+            want = _oracle_rc(orc.append_agents, layer, agents, counts, z, z, x, a)
+            try:
+                B.skv_project_append(ctx, layer, agents, counts, FAKE, FAKE, FAKE if with_a else None,
+                                     10000.0, FAKE); got = "OK"
             except B.SkvError as e:
                 got = e.code
         elif kind == "crop":
@@ -173,3 +190,43 @@ def test_counters_account_for_every_row():
     assert c["lr_rows"] == 30 and c["lr_zero_rows"] == 5
     assert c["rows_cropped"] == 3
     assert c["pages_alloc"] == 3 + 2 and c["pages_freed"] == 1
+
+
+def test_project_append_accounting_and_rotary_base_checks():
+    cfg = dict(CFG, mode=0, n_layers=1, page_size=4, max_pages=12)
+    ctx = make(cfg)
+    B.skv_append_base(ctx, 0, -1, FAKE, FAKE, n=6)
+    B.skv_crop(ctx, 0, 6)
+    before = B.skv_get_counters(ctx)["launches"]
+    B.skv_project_append(ctx, 0, [0, 2], [5, 3], FAKE, FAKE, FAKE, 500000.0, FAKE)
+    c = B.skv_get_counters(ctx)
+    assert c["launches"] == before + 1           # one fused launch for the whole call
+    assert c["base_rows_own"] == 8 and c["lr_rows"] == 8
+    assert B.skv_get_lens(ctx, 0)["S"] == [5, 0, 3] and B.skv_get_lens(ctx, 0)["lr_own"] == [5, 0, 3]
+    B.skv_project_append(ctx, 0, [1], [2], FAKE, FAKE, None, 0.0, FAKE)
+    assert B.skv_get_counters(ctx)["lr_zero_rows"] == 2
+    for bad in (1.0, 0.5, -1.0, float("inf"), float("nan")):
+        try:
+            B.skv_project_append(ctx, 0, [1], [1], FAKE, FAKE, None, bad, FAKE)
+            raise AssertionError(f"rotary base {bad} accepted")
+        except B.SkvError as e:
+            assert e.code == "ARG"
+    for bad in ((None, FAKE), (FAKE, None), (FAKE, FAKE + 2)):   # null, or overlapping buffers
+        try:
+            B.skv_pack_qkv(ctx, bad[0], bad[1])
+            raise AssertionError("bad pack arguments accepted")
+        except B.SkvError as e:
+            assert e.code == "ARG"
+    B.skv_pack_qkv(ctx, FAKE, FAKE + (1 << 22))
+    for args in ((None, FAKE, FAKE), (FAKE, None, FAKE), (FAKE, FAKE, None)):
+        try:
+            B.skv_project_append(ctx, 0, [1], [1], args[0], args[1], None, 0.0, args[2])
+            raise AssertionError("null pointer accepted")
+        except B.SkvError as e:
+            assert e.code == "ARG"
+    try:   # more pages than the pool holds: nothing appended
+        B.skv_project_append(ctx, 0, [1], [100], FAKE, FAKE, None, 0.0, FAKE)
+        raise AssertionError("overflow accepted")
+    except B.SkvError as e:
+        assert e.code == "OOM"
+    assert B.skv_get_lens(ctx, 0)["S"] == [5, 2, 3]
