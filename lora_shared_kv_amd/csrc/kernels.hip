@@ -1592,18 +1592,21 @@ static_assert(sizeof(ProjectParams) <= 4096, "kernel arguments");
 // measured: a third slot does not help and slows the split form).
 constexpr int kProjectSlots = 3;
 
-// SK (split K, for few rows): a workgroup takes one unit and one 16-row tile,
-// and its four waves take a quarter of the hidden columns each, with rings of
-// their own; the partial sums meet in LDS at the end. Four times as many
-// workgroups stream W as with four units per workgroup.
+// SK (split K, for few rows): a workgroup takes half a unit (one rotary-paired
+// pair of 16-feature tiles) and one 16-row tile, and its four waves take a
+// quarter of the hidden columns each, with rings of their own; the partial
+// sums meet in LDS at the end. Eight times as many workgroups stream W as with
+// four units per workgroup: the weight stream of a few rows is bound by how
+// many CUs pull on it.
 template <int D, int TM, bool SK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void project_kernel(ProjectParams p) {
   static_assert(!SK || TM == 16, "the split form takes 16-row tiles");
   constexpr int NC = TM / 16;           // 16-token tiles
   constexpr int NF = 2 * NC;            // X fragments (16 tokens x 32 columns) per 64-column stage
   constexpr int NS = kProjectSlots;
-  // u16 per ring slot: X fragments, then 8 W fragments per wave (SK: one wave's ring)
-  constexpr int SLOT = (NF + (SK ? 8 : 32)) * 512;
+  constexpr int NJ = SK ? 2 : 4;  // 16-feature tiles per wave
+  // u16 per ring slot: X fragments, then 2 NJ W fragments per wave (SK: one wave's ring)
+  constexpr int SLOT = (NF + (SK ? 2 * NJ : 8 * NJ)) * 512;
   constexpr int RING = (SK ? 4 : 1) * NS * SLOT * 2;
   static_assert(RING >= 64 * (128 + 8) * 2, "the low-rank blocks stage rows in the same LDS");
   extern __shared__ __attribute__((aligned(16))) u16 s_pr[];
@@ -1619,7 +1622,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int ug = lb / p.tok_tiles, tt = lb % p.tok_tiles;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, qd = lane >> 4;
-  const int unit = SK ? ug : ug * 4 + wave;
+  const int unit = SK ? ug / 2 : ug * 4 + wave;
+  const int half = SK ? ug % 2 : 0;  // SK: feature tiles half and half + 2 of the unit
   const bool active = unit < p.n_units;
   constexpr int UPH = D / 64;  // units per head
   const int uc = active ? unit : p.n_units - 1;
@@ -1637,11 +1641,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const __amdgpu_buffer_rsrc_t xr = byte_rsrc(p.x + (uint64_t)p.row0 * H, p.rows * H * 2);
   const int xoff0 = ((tt * TM + n) * H + 8 * qd) * 2;
 
-  f32x4 acc[NC][4];
+  // tile jj of the wave is feature tile j = jj (four per wave) or half + 2 jj (SK)
+  f32x4 acc[NC][NJ];
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[c][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int jj = 0; jj < NJ; ++jj) acc[c][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Copies of stage s into ring slot s % NS: this wave's share of the X
   // fragments, then its own eight W fragments. Stages past the end copy the
@@ -1663,20 +1668,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (void __attribute__((address_space(3)))*)(slot + fi * 512), 16,
                                                xoff0 + (16 * c * H + 64 * sc + 32 * ks) * 2, 0, 0, 0);
     }
-    u16* wdst = slot + (NF + (SK ? 0 : 8 * wave)) * 512;
+    u16* wdst = slot + (NF + (SK ? 0 : 2 * NJ * wave)) * 512;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (void __attribute__((address_space(3)))*)(wdst + (2 * j + ks) * 512),
+      for (int ks = 0; ks < 2; ++ks) {
+        const int j = SK ? half + 2 * jj : jj;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (void __attribute__((address_space(3)))*)(wdst + (2 * jj + ks) * 512),
                                                  16, ((sc * 8 + 2 * j + ks) * 64 + lane) * 16, 0, 0, 0);
+      }
   };
   // Before stage s: stages s .. s + NS - 2 are in flight (their X copies, then
   // 8 W copies each); with no more than NS - 2 stages' worth outstanding, all
   // of stage s's copies have landed (when the waves' X shares differ, 8 per
   // stage is the smaller count). The barrier publishes every wave's X copies
   // and retires the reads of the slot the next issue overwrites.
-  constexpr int kAfter = (NS - 2) * (SK ? NF + 8 : (NF % 4 == 0 ? 8 + NF / 4 : 8));
+  constexpr int kAfter = (NS - 2) * (SK ? NF + 2 * NJ : (NF % 4 == 0 ? 2 * NJ + NF / 4 : 2 * NJ));
   constexpr int kWaitStage = (kAfter & 15) | ((kAfter >> 4) << 14) | (7 << 4) | (15 << 8);
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) issue(s);
@@ -1685,43 +1692,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (!SK) __syncthreads();  // SK: every wave reads only its own ring
     issue(s + NS - 1);
     const u16* slot = ring + (s % NS) * SLOT;
-    bf16x8 bx[2][NC], aw[2][4];
+    bf16x8 bx[2][NC], aw[2][NJ];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        aw[ks][j] = *reinterpret_cast<const bf16x8*>(slot + (NF + (SK ? 0 : 8 * wave) + 2 * j + ks) * 512 + lane * 8);
+      for (int jj = 0; jj < NJ; ++jj)
+        aw[ks][jj] =
+            *reinterpret_cast<const bf16x8*>(slot + (NF + (SK ? 0 : 2 * NJ * wave) + 2 * jj + ks) * 512 + lane * 8);
 #pragma unroll
       for (int c = 0; c < NC; ++c) bx[ks][c] = *reinterpret_cast<const bf16x8*>(slot + (2 * c + ks) * 512 + lane * 8);
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
         for (int c = 0; c < NC; ++c)
-          acc[c][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[ks][j], bx[ks][c], acc[c][j], 0, 0, 0);
+          acc[c][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[ks][jj], bx[ks][c], acc[c][jj], 0, 0, 0);
     // every LDS read of the stage first, then the MFMAs (the first ones wait
     // only for their own operands)
-    __builtin_amdgcn_sched_group_barrier(0x100, 8 + 2 * NC, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 8 * NC, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NJ + 2 * NC, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NJ * NC, 0);
   }
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): no copy outlives the wave
   if constexpr (SK) {
     // waves 1..3 hand their partial sums to wave 0 (added in wave order)
     __syncthreads();  // every wave is done with its ring
-    float* red = reinterpret_cast<float*>(s_pr);  // [3][64 lanes][16]
+    float* red = reinterpret_cast<float*>(s_pr);  // [3][64 lanes][4 NJ]
     if (wave > 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<f32x4*>(red + ((wave - 1) * 64 + lane) * 16 + 4 * j) = acc[0][j];
+      for (int jj = 0; jj < NJ; ++jj)
+        *reinterpret_cast<f32x4*>(red + ((wave - 1) * 64 + lane) * 4 * NJ + 4 * jj) = acc[0][jj];
     }
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
     for (int w = 0; w < 3; ++w)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[0][j] += *reinterpret_cast<const f32x4*>(red + (w * 64 + lane) * 16 + 4 * j);
+      for (int jj = 0; jj < NJ; ++jj)
+        acc[0][jj] += *reinterpret_cast<const f32x4*>(red + (w * 64 + lane) * 4 * NJ + 4 * jj);
   }
   if (!active) return;
 
@@ -1741,13 +1750,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int slot_in_page = pos % kPage;
     const double view = (double)(p.view_off[s] + pos);
 #pragma unroll
-    for (int jp = 0; jp < 2; ++jp) {
+    for (int pp = 0; pp < NJ / 2; ++pp) {
+      // rotary pair: tiles jj = pp and pp + NJ/2 are feature tiles jp and jp + 2
+      const int jp = SK ? half : pp;
       const int dlo = 32 * hu + 16 * jp + 4 * qd;  // element 0 of the low half; the high half is + D/2
       float lo[4], hi[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        lo[e] = acc[c][jp][e];
-        hi[e] = acc[c][jp + 2][e];
+        lo[e] = acc[c][pp][e];
+        hi[e] = acc[c][pp + NJ / 2][e];
       }
       if (part < 2 && p.rope) {
 #pragma unroll
@@ -2039,7 +2050,7 @@ int dev_append(const Geometry& g, const AppendJob& job) {
 constexpr int kProjectSplitRows = 16;
 template <int D, int TM, bool SK>
 int launch_project_t(const Geometry& g, const ProjectParams& p) {
-  const size_t lds = (size_t)(SK ? 4 : 1) * kProjectSlots * (2 * TM / 16 + (SK ? 8 : 32)) * 512 * sizeof(u16);
+  const size_t lds = (size_t)(SK ? 4 : 1) * kProjectSlots * (2 * TM / 16 + (SK ? 4 : 32)) * 512 * sizeof(u16);
   // the ring exceeds the default dynamic LDS limit (set once per process)
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(project_kernel<D, TM, SK>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -2081,11 +2092,11 @@ int dev_project(const Geometry& g, const ProjectJob& job) {
   p.row0 = a.spans[0].src_row;
   p.rows = a.spans[a.n_spans - 1].src_row + a.spans[a.n_spans - 1].n - p.row0;
   p.n_units = (g.Hq + 2 * g.Hkv) * g.D / 64;
-  // up to 16 rows: one unit per workgroup (split K); more rows: four units
-  // and 64 rows per workgroup
+  // up to 16 rows: half a unit per workgroup (split K); more rows: four
+  // units and 64 rows per workgroup
   const int tm = p.rows <= kProjectSplitRows ? 16 : 64;
   p.tok_tiles = (p.rows + tm - 1) / tm;
-  p.n_gemm = (tm == 16 ? p.n_units : (p.n_units + 3) / 4) * p.tok_tiles;
+  p.n_gemm = (tm == 16 ? 2 * p.n_units : (p.n_units + 3) / 4) * p.tok_tiles;
   p.per_xcd = (p.n_gemm + 7) / 8;
   p.Hq = g.Hq;
   p.Hkv = g.Hkv;
