@@ -345,34 +345,77 @@ __device__ void append_lr_dot_block(const AppendParams& p, int s, int row, char*
 
 // Up to 64 low-rank rows with MFMA: C[row][rank] = X[row][:] . A[:][rank].
 // Wave w owns rows 16w..16w+15 of the tile; A is staged transposed in LDS,
-// kLrChunk hidden columns at a time, ranks padded to a multiple of 16.
+// kLrChunk hidden columns at a time, ranks padded to a multiple of 16. The
+// loads of chunk c + 1 (one row of A per thread as 16-byte vectors, and the
+// wave's eight x fragments) are issued before chunk c's MFMAs, so a chunk
+// waits on memory once at most.
 __device__ void append_lr_mfma_block(const AppendParams& p, int s, int tile, char* smem) {
   const skv::Span& sp = p.spans[s];
   const int r = p.r, H = p.hidden;
   const int NB = (r + 15) / 16;
   u16* at = reinterpret_cast<u16*>(smem);  // [NB*16][kLrChunk + 8]
   const int ldA = kLrChunk + 8;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int n = lane & 15, q = lane >> 4;
   const int row = tile * kLrTile + w * 16 + n;  // A-operand row of this lane
   const bool row_ok = row < sp.n;
   const u16* xrow = p.x + (uint64_t)(sp.src_row + (row_ok ? row : 0)) * H;
+  constexpr int kSteps = kLrChunk / 32;
+  static_assert(kLrChunk <= 256, "one row of A per thread");
+  const int nv = (r + 7) / 8;  // 16-byte vectors per row of A (r = 4: half of one)
+  u32x4 an[4];
+  bf16x8 xn[kSteps];
+  auto load_chunk = [&](int u0) {
+    const int cols = min(kLrChunk, H - u0);
+    if (t < cols) {
+      const u16* arow = sp.a + (uint64_t)(u0 + t) * r;
+      if (r >= 8) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (v < nv) an[v] = *reinterpret_cast<const u32x4*>(arow + 8 * v);
+      } else {
+        const u32x2 h = *reinterpret_cast<const u32x2*>(arow);
+        an[0] = u32x4{h[0], h[1], 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i) xn[i] = (row_ok && 32 * i < cols) ? ld8(xrow + u0 + 32 * i + 8 * q) : zero8();
+  };
   f32x4 acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+  load_chunk(0);
   for (int u0 = 0; u0 < H; u0 += kLrChunk) {
     const int cols = min(kLrChunk, H - u0);
-    __syncthreads();
-    for (int i = threadIdx.x; i < NB * 16 * cols; i += blockDim.x) {
-      int k = i / cols, u = i % cols;
-      at[k * ldA + u] = (k < r) ? sp.a[(uint64_t)(u0 + u) * r + k] : (u16)0;
+    u32x4 ac[4];
+    bf16x8 xc[kSteps];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) ac[v] = an[v];
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i) xc[i] = xn[i];
+    __syncthreads();  // the previous chunk's reads of at are done
+    if (t < cols) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k = 8 * v + 2 * e;
+          if (k < NB * 16) {
+            const uint32_t word = k < r ? ac[v][e] : 0u;
+            at[k * ldA + t] = (u16)(word & 0xffffu);
+            at[(k + 1) * ldA + t] = (u16)(word >> 16);
+          }
+        }
     }
     __syncthreads();
-    for (int s32 = 0; s32 < cols; s32 += 32) {
-      bf16x8 xa = row_ok ? ld8(xrow + u0 + s32 + 8 * q) : zero8();
+    if (u0 + kLrChunk < H) load_chunk(u0 + kLrChunk);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        if (nb < NB) {
-          bf16x8 ab = *reinterpret_cast<const bf16x8*>(at + (nb * 16 + n) * ldA + s32 + 8 * q);
-          acc[nb] = mfma(xa, ab, acc[nb]);
+    for (int i = 0; i < kSteps; ++i) {
+      if (32 * i < cols) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          if (nb < NB) {
+            bf16x8 ab = *reinterpret_cast<const bf16x8*>(at + (nb * 16 + n) * ldA + 32 * i + 8 * q);
+            acc[nb] = mfma(xc[i], ab, acc[nb]);
+          }
         }
       }
     }
