@@ -2091,8 +2091,8 @@ int dev_append(const Geometry& g, const AppendJob& job) {
 }
 
 // The GEMM part takes one 16-token tile in the split form for a few rows (a
-// decode step) and 64-token tiles otherwise (measured: the split form over
-// several row tiles is slower than 64-row tiles already at 64 rows).
+// decode step) and 32- or 64-token tiles otherwise (measured: the split form
+// over several row tiles is slower than 64-row tiles already at 64 rows).
 constexpr int kProjectSplitRows = 16;
 template <int D, int TM, bool SK>
 int launch_project_t(const Geometry& g, const ProjectParams& p) {
@@ -2110,7 +2110,8 @@ int launch_project_t(const Geometry& g, const ProjectParams& p) {
 
 template <int D>
 int launch_project(const Geometry& g, const ProjectParams& p, int tm) {
-  return tm == 16 ? launch_project_t<D, 16, true>(g, p) : launch_project_t<D, 64, false>(g, p);
+  if (tm == 16) return launch_project_t<D, 16, true>(g, p);
+  return tm == 32 ? launch_project_t<D, 32, false>(g, p) : launch_project_t<D, 64, false>(g, p);
 }
 
 int dev_pack_qkv(const Geometry& g, const uint16_t* w, uint16_t* out) {
@@ -2139,8 +2140,10 @@ int dev_project(const Geometry& g, const ProjectJob& job) {
   p.rows = a.spans[a.n_spans - 1].src_row + a.spans[a.n_spans - 1].n - p.row0;
   p.n_units = (g.Hq + 2 * g.Hkv) * g.D / 64;
   // up to 16 rows: half a unit per workgroup (split K); more rows: four
-  // units and 64 rows per workgroup
-  const int tm = p.rows <= kProjectSplitRows ? 16 : 64;
+  // units and 64 rows per workgroup, or 32 while 64-row tiles would not give
+  // every CU a workgroup (measured 1.25x faster at 64-512 rows, slower beyond)
+  const int groups = (p.n_units + 3) / 4;
+  const int tm = p.rows <= kProjectSplitRows ? 16 : (groups * ((p.rows + 63) / 64) < kCUs ? 32 : 64);
   p.tok_tiles = (p.rows + tm - 1) / tm;
   p.n_gemm = (tm == 16 ? 2 * p.n_units : (p.n_units + 3) / 4) * p.tok_tiles;
   p.per_xcd = (p.n_gemm + 7) / 8;
