@@ -87,6 +87,15 @@ def project_bytes(Hq, Hkv, d, hidden, r, rows, planes):
                 + rows * (Hq + 2 * Hkv) * d + rows * r)
 
 
+def project_kernel_name(Hq, Hkv, d, rows):
+    """Template arguments the library picks for a front-end call of one job:
+    the split form up to 16 rows, else 32-row tiles while 64-row tiles would
+    give fewer workgroups than the 256 CUs, else 64-row tiles."""
+    groups = ((Hq + 2 * Hkv) * d // 64 + 3) // 4
+    tm = 16 if rows <= 16 else (32 if groups * ((rows + 63) // 64) < 256 else 64)
+    return f"project_kernel<{d},{tm},{'true' if tm == 16 else 'false'}>"
+
+
 def frontend_timing(B, cfg, randn, reps=20):
     """Times skv_project_append on one layer (HIP events on the library's
     stream): one row per agent (the decode step's shape, bound by streaming the
@@ -135,7 +144,7 @@ def frontend_timing(B, cfg, randn, reps=20):
         by = project_bytes(Hq, Hkv, d, hidden, r, T, N if mode == 0 else 1)
         rec = {"rows": T, "avg_launch_us": round(us, 3), "flops": fl, "bytes": by,
                "tflops": round(fl / us / 1e6, 1), "gbs": round(by / us / 1e3, 1),
-               "kernel": f"project_kernel<{d},{16 if T <= 16 else 64},{'true' if T <= 16 else 'false'}>",
+               "kernel": project_kernel_name(Hq, Hkv, d, T),
                "hipblaslt_gemm_only_us": round(gemm_us, 3)}
         if T <= 16:
             rec.update(bound="hbm", peak=HBM_PEAK_GBS, unit="GB/s", frac=round(by / us / 1e3 / HBM_PEAK_GBS, 4))
