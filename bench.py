@@ -259,13 +259,15 @@ def main():
     ap.add_argument("--adapters", default=None, choices=["BaseShared", "BaseLRShared"],
                     help="adapter mode instead of the workload's (BaseShared: one A_i per agent)")
     ap.add_argument("--ttft", action="store_true",
-                    help="also time one new agent's first token: its rows and prefill on every layer")
+                    help="time one new agent's first token: its rows and prefill on every layer (the default)")
+    ap.add_argument("--no-ttft", action="store_true", help="skip the time-to-first-token leg")
     ap.add_argument("--mixed", type=int, default=0, metavar="K",
                     help="also time K mixed steps: the first half of the agents append and prefill 512 "
                          "own tokens while the second half decode one token, on every layer")
     ap.add_argument("--frontend", action="store_true",
-                    help="also time the fused front end (skv_project_append) on one layer of the workload: "
-                         "one row per agent (a decode step) and 512 rows of one agent (a suffix)")
+                    help="time the fused front end (skv_project_append) on one layer of the workload: "
+                         "one row per agent (a decode step) and 512 rows of one agent (a suffix) (the default)")
+    ap.add_argument("--no-frontend", action="store_true", help="skip the front-end leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
     args = ap.parse_args()
@@ -286,7 +288,8 @@ def main():
     G = Hq // Hkv
     total_steps = args.warmup + args.steps
     prefill_n = 512
-    own_max = args.warmup + 2 * args.steps + (0 if args.no_prefill else prefill_n) + args.mixed * (prefill_n + 1)
+    own_max = (args.warmup + 2 * args.steps + (0 if args.no_prefill else prefill_n) + args.mixed * (prefill_n + 1)
+               + (0 if args.no_ttft else prefill_n + 1))
     if private:
         max_pages = N * ((prefix + own_max) // 64 + 2) + 4
     else:
@@ -483,7 +486,7 @@ def main():
     # build its own copy of the prefix, so its rows and queries cover the whole
     # context ----
     ttft = None
-    if args.ttft:
+    if not args.no_ttft:
         a0 = [0]
         n_new = prefill_n + (prefix if private else 0)
         B.skv_crop(ctx, 0, 0 if private else prefix)
@@ -507,7 +510,7 @@ def main():
                 "queries_prefilled_per_layer": n_new}
 
     frontend = None
-    if args.frontend:
+    if not args.no_frontend:
         frontend = frontend_timing(B, dict(c, n_layers=1), randn, reps=20)
 
     if args.copy_calibration:
