@@ -69,3 +69,27 @@ def test_gpu_build_rejects_page_sizes_it_does_not_handle():
     with pytest.raises(B.SkvError) as e:
         B.skv_create(cfg, (1 << 20, 1 << 40), 0, "gpu")
     assert e.value.code == "UNSUPPORTED"
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the bench measures one GPU; asking for several must fail before any GPU work
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_bench_kernel_names_follow_the_library_choices():
+    # the template arguments bench.py reports must be the ones the library
+    # instantiates (decode split blocks, front-end tiles)
+    import bench
+    kernels = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                                "lora_shared_kv_amd", "csrc", "kernels.hip")).read()
+    assert bench.split_kernel_name(128, 16, 1, 8) == "decode_split_kernel<128,1,1>"
+    assert bench.project_kernel_name(32, 8, 128, 4) == "project_kernel<128,16,true>"
+    assert bench.project_kernel_name(32, 8, 128, 512) == "project_kernel<128,32,false>"
+    assert bench.project_kernel_name(32, 8, 128, 2048) == "project_kernel<128,64,false>"
+    for tm, sk in ((16, "true"), (32, "false"), (64, "false")):
+        assert f"launch_project_t<D, {tm}, {sk}>" in kernels
