@@ -156,7 +156,8 @@ int skv_pack_qkv(skv_ctx* ctx, const skv_bf16* w_qkv, skv_bf16* w_packed);
  *   x: device [sum counts][hidden], agent blocks in call order.
  *   w_packed: the layer's weights as packed by skv_pack_qkv.
  *   A: as in skv_append_agents, or NULL for adapter-off zero low-rank rows.
- *   rope_theta: rotary base, 0 = no rotation. Rotary embedding in the
+ *   rope_theta: rotary base, 0 = no rotation, else above 1 and finite
+ *     (ARG otherwise). Rotary embedding in the
  *     rotate-half form: for head vector u and view position t, each pair
  *     (u[j], u[j + d/2]), j < d/2, turns by the angle t * theta^(-2j/d). The
  *     view position of own row s of agent i is b_i + s (the shared prefix
