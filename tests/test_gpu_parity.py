@@ -270,6 +270,45 @@ def test_activation_offset_boundaries(shape_name):
     assert len(res) == 4
 
 
+def test_h1_session_with_offsets_and_accounting():
+    """A RoleKV-style session (RoleKV, "What it does" and "Challenges we ran
+    into"): agents take turns; each turn's adapter switches on after a 5-token
+    role header (its activation offset), the speaker appends and prefills its
+    rows and decodes; at the hand-off (H1) it crops its last 20 rows and
+    recomputes them as canonical rows (adapter off). Every attention call
+    matches the oracle, and the library's token accounting (rows appended,
+    low-rank rows, zero rows, rows cropped, pages) equals the oracle's
+    exactly, recompute included."""
+    from lora_shared_kv_amd import skv as B
+    R = _runner()
+    shape = synth.WORKLOADS["llama3"]
+    N = shape.n_agents
+    sc = synth.Schedule(shape, 1021, n_layers=1)
+    sc.draw_adapters()
+    sc.shared_prefix(1500)
+    agents = list(range(N))
+    for a in agents:
+        sc.attach(a)
+    for t in range(2 * N):
+        a = t % N
+        end = sc.b[a] + sc.S[0][a]
+        sc.set_lr_begin(a, end + 5)
+        sc.own_rows(0, [a], [40])
+        sc.attend("prefill", 0, [a], [16], tag=f"turn {t} prefill")
+        for k in range(3):
+            sc.decode_step(0, [a], tag=f"turn {t} step {k}")
+        end = sc.b[a] + sc.S[0][a]
+        sc.crop(a, end - 20)
+        sc.own_rows(0, [a], [20], lr="zero")
+    sc.attend("decode", 0, agents, [1] * N, tag="after the session")
+    gpu, orc, res = R.run_parity(sc, log=log)
+    assert len(res) == 2 * N * 4 + 1
+    got = B.skv_get_counters(gpu.ctx)
+    for k, v in orc.counters.items():
+        assert got[k] == v, (k, got[k], v)
+    assert orc.counters["rows_cropped"] == 2 * N * 20 and orc.counters["lr_zero_rows"] >= 2 * N * 20
+
+
 def test_lr_only_term():
     """V_base = 0: the output is only (P V_lr) B_i, about 10x smaller than usual."""
     R = _runner()
