@@ -1019,6 +1019,11 @@ __device__ __forceinline__ void dma_block(__amdgpu_buffer_rsrc_t r, int off, u16
                                            0, 0, 0);
 }
 
+// LDS (address space 3) views of the page ring: 32-bit addresses, so a read's
+// constant offset goes into the instruction's offset field.
+typedef __attribute__((address_space(3))) const u16 lds_u16;
+typedef __attribute__((address_space(3))) const bf16x8 lds_frag;
+
 // Suffix prefill: a workgroup of NW waves takes 16 NW RB query rows (rows =
 // query position x query head of one KV head) and streams the view's pages once: each page's K,
 // V^T and low-rank rows are copied to LDS by the whole workgroup through a ring
@@ -1037,6 +1042,16 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
   extern __shared__ __attribute__((aligned(16))) u16 s_kv[];  // [3][PE]
   __shared__ int32_t s_pages[kMaxViewPages];
   __shared__ float s_lr[NW][16][33];
+  // This lane's address in page buffer buf (elements lane_elems past its
+  // start), formed with one add and hidden from the optimiser by an empty asm:
+  // every operand read below is this address plus a constant the read
+  // encodes. Left visible, the compiler kept an address register per fragment
+  // and spent two adds on every read.
+  auto lane_ptr = [&](int buf, int lane_elems) {
+    lds_u16* ptr = (lds_u16*)(s_kv + buf * PE) + lane_elems;
+    asm volatile("" : "+v"(ptr));
+    return ptr;
+  };
   const int split = blockIdx.x / p.nblk;
   const int bid = blockIdx.x % p.nblk;  // blocks of one KV head share blockIdx mod Hkv (and an XCD)
   const int g = bid % p.Hkv;
@@ -1108,6 +1123,12 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
     const uint32_t one = ones_row && mb * 16 + n == p.r ? 0x3f803f80u : 0u;
     lr_ones[mb] = u32x4{one, one, one, one};
   }
+  // this lane's low-rank operand row of block mb in a page buffer: rank
+  // 16 mb + n (lanes past the last rank read the last one; masked above)
+  int lr_elems[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) lr_elems[mb] = 2 * 64 * D + min(mb * 16 + n, p.r - 1) * kPage + 8 * q;
+  auto lr_lane = [&](int mb, int buf) { return lane_ptr(buf, lr_elems[mb]); };
 
   // With LRO (some agent has an adapter activation offset), the low-rank rows
   // of keys before the agent's offset are masked out of the A operand; the
@@ -1208,14 +1229,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
   // products of page j - 1 (from its P), then the scores of page j
   auto mfma_phase = [&](int j) {
     if (j >= 1) {
-      const u16* kv = s_kv + ((j - 1) % 3) * PE;
+      lds_u16* kv = lane_ptr((j - 1) % 3, lane * 8);
       // O^T += V^T P^T and L^T += LR^T P^T; with a spare low-rank row, that
       // row is all ones and accumulates the row sums
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(kv + 64 * D + (h * DB + db) * 512 + lane * 8);
+          const bf16x8 vf = *reinterpret_cast<lds_frag*>(kv + 64 * D + (h * DB + db) * 512);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma(vf, pt[rb][h], oacc[rb][db]);
         }
@@ -1223,8 +1244,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int k = min(mb * 16 + n, p.r - 1);
-          const u32x4 raw = *reinterpret_cast<const u32x4*>(kv + 2 * 64 * D + k * kPage + h * 32 + 8 * q);
+          const u32x4 raw = __builtin_bit_cast(u32x4, *reinterpret_cast<lds_frag*>(lr_lane(mb, (j - 1) % 3) + h * 32));
           const u32x4 keep = LRO ? lr_keep(j - 1, h) : u32x4{~0u, ~0u, ~0u, ~0u};
           const bf16x8 lf = __builtin_bit_cast(bf16x8, (raw & lr_mask[mb] & keep) | lr_ones[mb]);
 #pragma unroll
@@ -1232,14 +1252,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
         }
     }
     if (j < n_pages) {
-      const u16* kv = s_kv + (j % 3) * PE;
+      lds_u16* kv = lane_ptr(j % 3, lane * 8);
       // S^T = K Q^T for the page's 64 keys and the RB row blocks, one 16-key
       // score tile (half h, tile t: index 2h + t) at a time
 #pragma unroll
       for (int ht = 0; ht < 4; ++ht) {
         bf16x8 kf[KS];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(kv + (ht * KS + s) * 512 + lane * 8);
+        for (int s = 0; s < KS; ++s) kf[s] = *reinterpret_cast<lds_frag*>(kv + (ht * KS + s) * 512);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           f32x4 acc = {0, 0, 0, 0};
@@ -1267,18 +1287,17 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
   static_assert(NC <= NF, "copies ride along the fragments");
   static_assert(PF % RB == 0 && kAhead <= 15, "prefetch split");
   bf16x8 vpre[PF];
-  auto frag_load = [&](int f, const u16* kvp, const u16* kvc) -> bf16x8 {
+  auto frag_load = [&](int f, lds_u16* kvp, lds_u16* const* kvl, lds_u16* kvc) -> bf16x8 {
     if (f < NV)  // V^T tile: half h = f / DB, column block db = f % DB
-      return *reinterpret_cast<const bf16x8*>(kvp + 64 * D + f * 512 + lane * 8);
+      return *reinterpret_cast<lds_frag*>(kvp + 64 * D + f * 512);
     if (f < NV + NL) {  // low-rank rows: block mb, half h
       const int mb = (f - NV) >> 1, h = (f - NV) & 1;
-      const int k = min(mb * 16 + n, p.r - 1);
-      return *reinterpret_cast<const bf16x8*>(kvp + 2 * 64 * D + k * kPage + h * 32 + 8 * q);
+      return *reinterpret_cast<lds_frag*>(kvl[mb] + h * 32);
     }
     // K tile (ht, s), taken chunk-major (s outer) so that consecutive MFMAs
     // update different score tiles
     const int ks = f - NV - NL, ht = ks % 4, s = ks / 4;
-    return *reinterpret_cast<const bf16x8*>(kvc + (ht * KS + s) * 512 + lane * 8);
+    return *reinterpret_cast<lds_frag*>(kvc + (ht * KS + s) * 512);
   };
   auto frag_use = [&](int f, bf16x8 x) {
     if (f < NV) {
@@ -1303,8 +1322,11 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
       keep_lr[0] = lr_keep(j - 1, 0);
       keep_lr[1] = lr_keep(j - 1, 1);
     }
-    const u16* kvp = s_kv + ((j - 1) % 3) * PE;
-    const u16* kvc = s_kv + (j % 3) * PE;
+    lds_u16* kvp = lane_ptr((j - 1) % 3, lane * 8);
+    lds_u16* kvc = lane_ptr(j % 3, lane * 8);
+    lds_u16* kvl[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) kvl[mb] = lr_lane(mb, (j - 1) % 3);
     PageSrc src{};
     if (WC) src = page_src(src_page);
     u16* dst = s_kv + dst_buf * PE;
@@ -1315,13 +1337,13 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
     // order of use and each wait covers just the fragment needed
 #pragma unroll
     for (int f = PF; f < kAhead && f < NF; ++f) {
-      fr[f] = frag_load(f, kvp, kvc);
+      fr[f] = frag_load(f, kvp, kvl, kvc);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int g = f + kAhead;
-      if (g >= PF && g < NF) fr[g] = frag_load(g, kvp, kvc);
+      if (g >= PF && g < NF) fr[g] = frag_load(g, kvp, kvl, kvc);
       frag_use(f, fr[f]);
       if (WC && f < NC) copy_one(f, src, dst);
       __builtin_amdgcn_sched_barrier(0);
@@ -1338,7 +1360,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
   // divides by the sum of the same P, so the result does not depend on m.
   constexpr float kSlack = 8.f;
   auto softmax_phase = [&](int i) {
-    const u16* kvi = s_kv + (i % 3) * PE + 64 * D;  // V^T tile of page i
+    lds_u16* kvi = lane_ptr(i % 3, lane * 8) + 64 * D;  // V^T tile of page i
     const int ia = p_lo + i;                         // the view's page
     const bool own = ia >= np_sh;
     const int pg_key0 = (own ? ia - np_sh : ia) * kPage;  // first key of the page in its segment
@@ -1376,7 +1398,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
       // bounded rate, so a burst of them would stall the wave)
       constexpr int PV = PF / RB;
 #pragma unroll
-      for (int f = rb * PV; f < (rb + 1) * PV; ++f) vpre[f] = *reinterpret_cast<const bf16x8*>(kvi + f * 512 + lane * 8);
+      for (int f = rb * PV; f < (rb + 1) * PV; ++f) vpre[f] = *reinterpret_cast<lds_frag*>(kvi + f * 512);
       float pv[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e)
