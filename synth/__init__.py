@@ -411,8 +411,11 @@ def qwen3_schedule(takeover=160, seed=1002, n_layers=1, decode=64, **kw) -> Sche
     return sc
 
 
-def llama3_schedule(prefix=33792, seed=1003, n_layers=1, decode=256, fused=False, **kw) -> Schedule:
-    """Shared-A agents decode one token each per step over a long shared trajectory."""
+def llama3_schedule(prefix=33792, seed=1003, n_layers=1, decode=256, fused=False, prefill=0,
+                    **kw) -> Schedule:
+    """Shared-A agents decode one token each per step over a long shared trajectory;
+    with prefill > 0 each agent first appends that many own tokens and they are
+    prefilled together (the suffix-prefill shape of the throughput run)."""
     s = LLAMA3.with_(prefix=prefix)
     sc = Schedule(s, seed, n_layers, **kw)
     sc.draw_adapters()
@@ -420,6 +423,10 @@ def llama3_schedule(prefix=33792, seed=1003, n_layers=1, decode=256, fused=False
     agents = list(range(s.n_agents))
     for a in agents:
         sc.attach(a)
+    if prefill:
+        for l in range(sc.L):
+            sc.own_rows(l, agents, [prefill] * len(agents))
+            sc.attend("prefill", l, agents, [prefill] * len(agents), tag="suffix prefill")
     for t in range(decode):
         for l in range(sc.L):
             if fused:

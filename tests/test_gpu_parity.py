@@ -147,6 +147,17 @@ def test_qwen3_takeover(takeover):
                  log=log)
 
 
+def test_llama3_suffix_prefill_at_32k():
+    """The suffix prefill the throughput run times (4 agents x 512 own tokens over
+    the 32,768-token shared prefix, llama3 shapes, one launch of 256 row blocks),
+    on sampled query rows, then two fused decode steps on the same cache."""
+    R = _runner()
+    sc = synth.llama3_schedule(prefix=32768, prefill=512, decode=2, fused=True)
+    samp = lambda ev: (list(range(0, sum(ev.n_q), 61)) + [sum(ev.n_q) - 1]) if ev.kind == "prefill" else None
+    _, _, res = R.run_parity(sc, sample_rows=samp, log=log)
+    assert sum(1 for r in res if r[1] == "prefill") == 1
+
+
 @pytest.mark.parametrize("prefix,steps", [(33792, 3), (67584, 2)])
 def test_llama3_long_prefix_decode(prefix, steps):
     R = _runner()
