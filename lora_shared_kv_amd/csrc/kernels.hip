@@ -200,8 +200,7 @@ struct AppendParams {
   int lr_kind[skv::kMaxJobSpans];        // 0 zero rows, 1 dot product per row, 2 MFMA tiles
 };
 
-constexpr int kLrTile = 64;   // rows per MFMA low-rank block
-constexpr int kLrChunk = 256; // hidden columns of A staged in LDS per step
+constexpr int kLrTile = 16;  // rows per MFMA low-rank block
 
 template <int D>
 __device__ void append_kv_tile(const AppendParams& p, int s, int blk, char* smem) {
@@ -343,91 +342,133 @@ __device__ void append_lr_dot_block(const AppendParams& p, int s, int row, char*
   }
 }
 
-// Up to 64 low-rank rows with MFMA: C[row][rank] = X[row][:] . A[:][rank].
-// Wave w owns rows 16w..16w+15 of the tile; A is staged transposed in LDS,
-// kLrChunk hidden columns at a time, ranks padded to a multiple of 16. The
-// loads of chunk c + 1 (one row of A per thread as 16-byte vectors, and the
-// wave's eight x fragments) are issued before chunk c's MFMAs, so a chunk
-// waits on memory once at most.
+// Up to 16 low-rank rows with MFMA: C[row][rank] = X[row][:] . A[:][rank].
+// The four waves split the hidden columns into 128-column slabs (wave w takes
+// slabs w, w + 4, ...) and keep two slabs' loads in flight: the slab's rows
+// of A (a row per lane and 64-column half, 16-byte vectors) and the wave's
+// X fragments. A wave stages each 64-column half of A transposed in its own
+// LDS region (ranks padded to a multiple of 16) and reads the MFMA operand
+// back from it; only its own lanes touch the region, and a wave's LDS
+// operations complete in program order. The four partial tiles are added
+// through LDS at the end.
+constexpr int kLrStage = 64 + 4;  // u16 per staged rank row of a wave's region
+
 __device__ void append_lr_mfma_block(const AppendParams& p, int s, int tile, char* smem) {
   const skv::Span& sp = p.spans[s];
   const int r = p.r, H = p.hidden;
   const int NB = (r + 15) / 16;
-  u16* at = reinterpret_cast<u16*>(smem);  // [NB*16][kLrChunk + 8]
-  const int ldA = kLrChunk + 8;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = lane & 15, q = lane >> 4;
-  const int row = tile * kLrTile + w * 16 + n;  // A-operand row of this lane
+  const int row = tile * kLrTile + n;  // A-operand row of this lane
   const bool row_ok = row < sp.n;
   const u16* xrow = p.x + (uint64_t)(sp.src_row + (row_ok ? row : 0)) * H;
-  constexpr int kSteps = kLrChunk / 32;
-  static_assert(kLrChunk <= 256, "one row of A per thread");
+  u16* const at = reinterpret_cast<u16*>(smem) + w * 32 * kLrStage;  // [NB*16][kLrStage]
+  const int nslab = (H + 127) / 128;
+  const int mine = w < nslab ? (nslab - 1 - w) / 4 + 1 : 0;
   const int nv = (r + 7) / 8;  // 16-byte vectors per row of A (r = 4: half of one)
-  u32x4 an[4];
-  bf16x8 xn[kSteps];
-  auto load_chunk = [&](int u0) {
-    const int cols = min(kLrChunk, H - u0);
-    if (t < cols) {
-      const u16* arow = sp.a + (uint64_t)(u0 + t) * r;
-      if (r >= 8) {
+  struct Slab {
+    u32x4 a[2][4];  // [half][vector]
+    bf16x8 x[4];    // [half * 2 + k-step]
+  };
+  auto load = [&](int i, Slab& sl) {
+    const int c0 = 128 * (w + 4 * i);
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (v < nv) an[v] = *reinterpret_cast<const u32x4*>(arow + 8 * v);
-      } else {
-        const u32x2 h = *reinterpret_cast<const u32x2*>(arow);
-        an[0] = u32x4{h[0], h[1], 0u, 0u};
+    for (int h = 0; h < 2; ++h) {
+      const int c = c0 + 64 * h;
+      if (c < H) {  // H is a multiple of 64: a half is all in or all out
+        const u16* arow = sp.a + (uint64_t)(c + lane) * r;
+        if (r >= 8) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (v < nv) sl.a[h][v] = *reinterpret_cast<const u32x4*>(arow + 8 * v);
+        } else {
+          const u32x2 t = *reinterpret_cast<const u32x2*>(arow);
+          sl.a[h][0] = u32x4{t[0], t[1], 0u, 0u};
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) sl.x[2 * h + ks] = row_ok ? ld8(xrow + c + 32 * ks + 8 * q) : zero8();
       }
     }
-#pragma unroll
-    for (int i = 0; i < kSteps; ++i) xn[i] = (row_ok && 32 * i < cols) ? ld8(xrow + u0 + 32 * i + 8 * q) : zero8();
   };
   f32x4 acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-  load_chunk(0);
-  for (int u0 = 0; u0 < H; u0 += kLrChunk) {
-    const int cols = min(kLrChunk, H - u0);
-    u32x4 ac[4];
-    bf16x8 xc[kSteps];
+  auto compute = [&](int i, const Slab& sl) {
+    const int c0 = 128 * (w + 4 * i);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) ac[v] = an[v];
-#pragma unroll
-    for (int i = 0; i < kSteps; ++i) xc[i] = xn[i];
-    __syncthreads();  // the previous chunk's reads of at are done
-    if (t < cols) {
+    for (int h = 0; h < 2; ++h) {
+      if (c0 + 64 * h >= H) break;
 #pragma unroll
       for (int v = 0; v < 4; ++v)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int k = 8 * v + 2 * e;
           if (k < NB * 16) {
-            const uint32_t word = k < r ? ac[v][e] : 0u;
-            at[k * ldA + t] = (u16)(word & 0xffffu);
-            at[(k + 1) * ldA + t] = (u16)(word >> 16);
+            const uint32_t word = k < r ? sl.a[h][v][e] : 0u;
+            at[k * kLrStage + lane] = (u16)(word & 0xffffu);
+            at[(k + 1) * kLrStage + lane] = (u16)(word >> 16);
           }
         }
-    }
-    __syncthreads();
-    if (u0 + kLrChunk < H) load_chunk(u0 + kLrChunk);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-    for (int i = 0; i < kSteps; ++i) {
-      if (32 * i < cols) {
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
+        for (int nb = 0; nb < 2; ++nb)
           if (nb < NB) {
-            bf16x8 ab = *reinterpret_cast<const bf16x8*>(at + (nb * 16 + n) * ldA + 32 * i + 8 * q);
-            acc[nb] = mfma(xc[i], ab, acc[nb]);
+            const bf16x8 ab = *reinterpret_cast<const bf16x8*>(at + (nb * 16 + n) * kLrStage + 32 * ks + 8 * q);
+            acc[nb] = mfma(sl.x[2 * h + ks], ab, acc[nb]);
           }
-        }
-      }
+      // the next half's transposed writes follow these reads in program order
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  };
+  if (mine > 0) {
+    Slab A, Bf;
+    load(0, A);
+    int i = 0;
+    // sched_barrier keeps each prefetch ahead of the wait for the slab in use
+    for (; i + 2 < mine; i += 2) {
+      load(i + 1, Bf);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(i, A);
+      load(i + 2, A);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(i + 1, Bf);
+    }
+    if (mine - i == 2) {
+      load(i + 1, Bf);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(i, A);
+      compute(i + 1, Bf);
+    } else {
+      compute(i, A);
     }
   }
-  // C tile: lane holds rank 16nb + n, rows 16w + 4q + j of the tile
+  // waves 1..3 hand their partial tiles to wave 0 (added in wave order)
+  __syncthreads();  // every wave is done with its staging region
+  float* const red = reinterpret_cast<float*>(smem);  // [3][64 lanes][8]
+  if (w > 0) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      if (nb < NB) *reinterpret_cast<f32x4*>(red + ((w - 1) * 64 + lane) * 8 + 4 * nb) = acc[nb];
+  }
+  __syncthreads();
+  if (w != 0) return;
+#pragma unroll
+  for (int ww = 0; ww < 3; ++ww)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      if (nb < NB) acc[nb] += *reinterpret_cast<const f32x4*>(red + (ww * 64 + lane) * 8 + 4 * nb);
+  // C tile: lane holds rank 16nb + n, rows 4q + j of the tile
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int k = nb * 16 + n;
     if (nb < NB && k < r) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int rr = tile * kLrTile + w * 16 + 4 * q + j;
+        const int rr = tile * kLrTile + 4 * q + j;
         if (rr < sp.n) {
           const int pos = sp.pos0 + rr;
           const int page = p.ids[sp.ids_off + pos / kPage - sp.first_page];
