@@ -343,69 +343,73 @@ __device__ void append_lr_dot_block(const AppendParams& p, int s, int row, char*
 }
 
 // Up to 16 low-rank rows with MFMA: C[row][rank] = X[row][:] . A[:][rank].
-// The four waves split the hidden columns into 128-column slabs (wave w takes
-// slabs w, w + 4, ...) and keep two slabs' loads in flight: the slab's rows
-// of A (a row per lane and 64-column half, 16-byte vectors) and the wave's
-// X fragments. A wave stages each 64-column half of A transposed in its own
-// LDS region (ranks padded to a multiple of 16) and reads the MFMA operand
-// back from it; only its own lanes touch the region, and a wave's LDS
-// operations complete in program order. The four partial tiles are added
-// through LDS at the end.
+// The four waves split the hidden columns into slabs of HS 64-column sections
+// (wave w takes slabs w, w + 4, ...) and keep two slabs' loads in flight: the
+// slab's rows of A (a row per lane and section: NV 16-byte vectors, or 8
+// bytes when NV = 0 for rank 4) and the wave's X fragments. Every load is
+// unconditional, so the compiler's waits count exactly: lanes past the last
+// row read the span's first row (their output rows are never stored), and a
+// section past the last column reads the last one (its products are skipped).
+// A wave stages each 64-column section of A transposed in its own LDS region
+// (ranks padded to a multiple of 16) and reads the MFMA operand back from it;
+// only its own lanes touch the region, and a wave's LDS operations complete in
+// program order. The four partial tiles are added through LDS at the end.
 constexpr int kLrStage = 64 + 4;  // u16 per staged rank row of a wave's region
 
+template <int NV, int HS>
 __device__ void append_lr_mfma_block(const AppendParams& p, int s, int tile, char* smem) {
+  constexpr int R = NV == 0 ? 4 : 8 * NV;  // rank
+  constexpr int NB = (R + 15) / 16;        // 16-rank blocks
   const skv::Span& sp = p.spans[s];
-  const int r = p.r, H = p.hidden;
-  const int NB = (r + 15) / 16;
+  const int H = p.hidden;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = lane & 15, q = lane >> 4;
   const int row = tile * kLrTile + n;  // A-operand row of this lane
-  const bool row_ok = row < sp.n;
-  const u16* xrow = p.x + (uint64_t)(sp.src_row + (row_ok ? row : 0)) * H;
+  const u16* xrow = p.x + (uint64_t)(sp.src_row + (row < sp.n ? row : 0)) * H;
   u16* const at = reinterpret_cast<u16*>(smem) + w * 32 * kLrStage;  // [NB*16][kLrStage]
-  const int nslab = (H + 127) / 128;
+  const int nslab = (H + 64 * HS - 1) / (64 * HS);
   const int mine = w < nslab ? (nslab - 1 - w) / 4 + 1 : 0;
-  const int nv = (r + 7) / 8;  // 16-byte vectors per row of A (r = 4: half of one)
   struct Slab {
-    u32x4 a[2][4];  // [half][vector]
-    bf16x8 x[4];    // [half * 2 + k-step]
+    u32x4 a[HS][NV == 0 ? 1 : NV];  // [section][vector]
+    bf16x8 x[2 * HS];                // [section * 2 + k-step]
   };
   auto load = [&](int i, Slab& sl) {
-    const int c0 = 128 * (w + 4 * i);
+    const int c0 = 64 * HS * (w + 4 * i);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = c0 + 64 * h;
-      if (c < H) {  // H is a multiple of 64: a half is all in or all out
-        const u16* arow = sp.a + (uint64_t)(c + lane) * r;
-        if (r >= 8) {
+    for (int h = 0; h < HS; ++h) {
+      const int c = min(c0 + 64 * h, H - 64);  // H is a multiple of 64
+      const u16* arow = sp.a + (uint64_t)(c + lane) * R;
+      if constexpr (NV == 0) {
+        const u32x2 t = *reinterpret_cast<const u32x2*>(arow);
+        sl.a[h][0] = u32x4{t[0], t[1], 0u, 0u};
+      } else {
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (v < nv) sl.a[h][v] = *reinterpret_cast<const u32x4*>(arow + 8 * v);
-        } else {
-          const u32x2 t = *reinterpret_cast<const u32x2*>(arow);
-          sl.a[h][0] = u32x4{t[0], t[1], 0u, 0u};
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) sl.x[2 * h + ks] = row_ok ? ld8(xrow + c + 32 * ks + 8 * q) : zero8();
+        for (int v = 0; v < NV; ++v) sl.a[h][v] = *reinterpret_cast<const u32x4*>(arow + 8 * v);
       }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) sl.x[2 * h + ks] = ld8(xrow + c + 32 * ks + 8 * q);
     }
   };
-  f32x4 acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-  auto compute = [&](int i, const Slab& sl) {
-    const int c0 = 128 * (w + 4 * i);
+  f32x4 acc[NB];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0, 0, 0, 0};
+  // staged rank rows the A vectors do not cover (padding up to NB*16) hold zeros
+  constexpr int kCovered = NV == 0 ? 8 : 8 * NV;
+#pragma unroll
+  for (int k = kCovered; k < NB * 16; ++k) at[k * kLrStage + lane] = 0;
+  auto compute = [&](int i, const Slab& sl) {
+    const int c0 = 64 * HS * (w + 4 * i);
+#pragma unroll
+    for (int h = 0; h < HS; ++h) {
       if (c0 + 64 * h >= H) break;
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
+      for (int v = 0; v < (NV == 0 ? 1 : NV); ++v)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int k = 8 * v + 2 * e;
-          if (k < NB * 16) {
-            const uint32_t word = k < r ? sl.a[h][v][e] : 0u;
-            at[k * kLrStage + lane] = (u16)(word & 0xffffu);
-            at[(k + 1) * kLrStage + lane] = (u16)(word >> 16);
-          }
+          const uint32_t word = k < R ? sl.a[h][v][e] : 0u;
+          at[k * kLrStage + lane] = (u16)(word & 0xffffu);
+          at[(k + 1) * kLrStage + lane] = (u16)(word >> 16);
         }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -413,12 +417,11 @@ __device__ void append_lr_mfma_block(const AppendParams& p, int s, int tile, cha
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          if (nb < NB) {
-            const bf16x8 ab = *reinterpret_cast<const bf16x8*>(at + (nb * 16 + n) * kLrStage + 32 * ks + 8 * q);
-            acc[nb] = mfma(sl.x[2 * h + ks], ab, acc[nb]);
-          }
-      // the next half's transposed writes follow these reads in program order
+        for (int nb = 0; nb < NB; ++nb) {
+          const bf16x8 ab = *reinterpret_cast<const bf16x8*>(at + (nb * 16 + n) * kLrStage + 32 * ks + 8 * q);
+          acc[nb] = mfma(sl.x[2 * h + ks], ab, acc[nb]);
+        }
+      // the next section's transposed writes follow these reads in program order
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -451,28 +454,26 @@ __device__ void append_lr_mfma_block(const AppendParams& p, int s, int tile, cha
   float* const red = reinterpret_cast<float*>(smem);  // [3][64 lanes][8]
   if (w > 0) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-      if (nb < NB) *reinterpret_cast<f32x4*>(red + ((w - 1) * 64 + lane) * 8 + 4 * nb) = acc[nb];
+    for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<f32x4*>(red + ((w - 1) * 64 + lane) * 8 + 4 * nb) = acc[nb];
   }
   __syncthreads();
   if (w != 0) return;
 #pragma unroll
   for (int ww = 0; ww < 3; ++ww)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-      if (nb < NB) acc[nb] += *reinterpret_cast<const f32x4*>(red + (ww * 64 + lane) * 8 + 4 * nb);
+    for (int nb = 0; nb < NB; ++nb) acc[nb] += *reinterpret_cast<const f32x4*>(red + (ww * 64 + lane) * 8 + 4 * nb);
   // C tile: lane holds rank 16nb + n, rows 4q + j of the tile
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
     const int k = nb * 16 + n;
-    if (nb < NB && k < r) {
+    if (k < R) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int rr = tile * kLrTile + 4 * q + j;
         if (rr < sp.n) {
           const int pos = sp.pos0 + rr;
           const int page = p.ids[sp.ids_off + pos / kPage - sp.first_page];
-          p.LRT[sp.plane * p.lr_plane + (uint64_t)page * r * kPage + k * kPage + pos % kPage] =
+          p.LRT[sp.plane * p.lr_plane + (uint64_t)page * R * kPage + k * kPage + pos % kPage] =
               f2bf(acc[nb][j]);
         }
       }
@@ -481,7 +482,11 @@ __device__ void append_lr_mfma_block(const AppendParams& p, int s, int tile, cha
 }
 
 // Work of block b of an append job (block 0 also writes the new page-table
-// entries). smem must hold at least 64 * (128 + 8) bf16.
+// entries). smem must hold at least 64 * (128 + 8) bf16. KV and MFMA_LR say
+// whether the kernel carries the K/V tile copies and the MFMA low-rank tiles:
+// launches whose jobs never hold such blocks leave that code out, which keeps
+// them small (the host checks the jobs it gives them).
+template <bool KV = true, bool MFMA_LR = true>
 __device__ void append_block(const AppendParams& p, int b, char* smem) {
   if (b == 0 && p.update_tables) {
     for (int s = 0; s < p.n_spans; ++s) {
@@ -493,9 +498,11 @@ __device__ void append_block(const AppendParams& p, int b, char* smem) {
   const int n_kv = p.kv_block0[p.n_spans];
   if (b >= n_kv + p.lr_block0[p.n_spans]) return;
   if (b < n_kv) {
-    int s = 0;
-    while (b >= p.kv_block0[s + 1]) ++s;
-    append_kv_block(p, s, b - p.kv_block0[s], smem);
+    if constexpr (KV) {
+      int s = 0;
+      while (b >= p.kv_block0[s + 1]) ++s;
+      append_kv_block(p, s, b - p.kv_block0[s], smem);
+    }
     return;
   }
   b -= n_kv;
@@ -506,8 +513,16 @@ __device__ void append_block(const AppendParams& p, int b, char* smem) {
     append_lr_zero_block(p, s, sub);
   else if (p.lr_kind[s] == 1)
     append_lr_dot_block(p, s, sub, smem);
-  else
-    append_lr_mfma_block(p, s, sub, smem);
+  else if constexpr (MFMA_LR) {
+    if (p.r == 4)
+      append_lr_mfma_block<0, 4>(p, s, sub, smem);
+    else if (p.r == 8)
+      append_lr_mfma_block<1, 4>(p, s, sub, smem);
+    else if (p.r == 16)
+      append_lr_mfma_block<2, 4>(p, s, sub, smem);
+    else
+      append_lr_mfma_block<4, 2>(p, s, sub, smem);
+  }
 }
 
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
@@ -612,7 +627,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
   if ((int)blockIdx.x < p.n_app) {
     // fused decode step: write the new low-rank rows and page-table entries;
     // the items below read only keys cached before this step
-    append_block(p.app, blockIdx.x, reinterpret_cast<char*>(s_buf));
+    append_block<false, false>(p.app, blockIdx.x, reinterpret_cast<char*>(s_buf));
     return;
   }
   const int item = blockIdx.x - p.n_app;
@@ -906,7 +921,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
   if ((int)blockIdx.x >= p.n_rows) {
     // fused decode step: copy the new K/V rows into the pages; the rows merged
     // here take the new token from the step's inputs instead
-    append_block(p.app, blockIdx.x - p.n_rows, s_app);
+    append_block<true, false>(p.app, blockIdx.x - p.n_rows, s_app);
     return;
   }
   __shared__ float s_w[kMaxMergeSlots];
@@ -2295,6 +2310,14 @@ static int decode_impl(const Geometry& g, const AttnJob& job, const AppendJob* a
       sub.update_tables = false;
       plan_append(g, sub, kv_app);
       n_kv_app = append_blocks(kv_app);
+      // the split launch's append code has no K/V copies and no MFMA low-rank
+      // tiles, the merge launch's no low-rank rows at all
+      bool fits = p.app.kv_block0[p.app.n_spans] == 0 && kv_app.lr_block0[kv_app.n_spans] == 0;
+      for (int s = 0; s < p.app.n_spans; ++s) fits = fits && p.app.lr_kind[s] != 2;
+      if (!fits) {
+        snprintf(g_err, sizeof g_err, "decode step: an agent appends more than one row");
+        return SKV_ERR_UNSUPPORTED;
+      }
     }
     // flattened key sequence per KV head: shared prefix, then each own suffix,
     // each padded to whole 32-key chunks
