@@ -432,6 +432,32 @@ def test_one_hot_x_gives_rows_of_A_exactly():
         assert np.array_equal(row, a[(5 * i) % 128]), i
 
 
+@pytest.mark.parametrize("hidden,rank,n", [(64, 4, 9), (192, 32, 17), (320, 16, 40), (192, 8, 31)])
+def test_lowrank_rows_at_slab_edges(hidden, rank, n):
+    """The MFMA low-rank tiles (16 rows each; the hidden columns go to the four
+    waves in slabs) at hidden sizes that end inside a slab or give some waves
+    no slab, at every rank, with row counts around the tile edges. Each row is
+    within one bf16 ulp of the oracle's exact X A, plus the fp32 sum's error
+    (2^-20 sum |x_k a_k|, which near a cancellation exceeds an ulp of the
+    small result)."""
+    from lora_shared_kv_amd import skv as B
+    R = _runner()
+    shape = Shape("e", 1, 4, 2, 64, hidden, rank, 1, BASE_SHARED, 0)
+    sc = Schedule(shape, 11 + hidden + rank, n_layers=1)
+    sc.draw_adapters()
+    sc.shared_prefix(n)
+    gpu, orc, _ = R.run_parity(sc)
+    _, _, LRT = (t.cpu().numpy().view(np.uint16) for t in _pool_views(gpu))
+    pages = B.skv_get_pages(gpu.ctx, 0, -1)
+    ev = next(e for e in sc.events if isinstance(e, synth.AppendLowrank))
+    ref = orc.lr[0][-1][0].get(n)
+    got = bf16_bits_to_f64(np.stack([LRT[0, 0, pages[j // 64], :, j % 64] for j in range(n)]))
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+    sum_err = 2.0 ** -20 * (np.abs(bf16_bits_to_f64(ev.x)) @ np.abs(bf16_bits_to_f64(ev.a)))
+    assert got.shape == (n, rank)
+    assert np.all(np.abs(got - ref) <= ulp + sum_err), np.max(np.abs(got - ref) / ulp)
+
+
 def test_decode_is_deterministic():
     import torch
     from lora_shared_kv_amd import skv as B
