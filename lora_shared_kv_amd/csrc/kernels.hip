@@ -1611,6 +1611,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
 // prefill workgroup shape: waves, and 16-row blocks per wave
 constexpr int kPrefNW = 8;
 constexpr int kPrefRB = 2;
+constexpr int kMaxPrefillSplit = 8;  // key ranges a prefill row block is split into, at most
 
 // Merge of a split prefill: one wave per query row combines the partial rows
 // of its key ranges (s = 0 .. ksplit - 1 at part[((s nblk + block) 256 + row)
@@ -1640,11 +1641,29 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillMergeParams p
   const int rho = qb * ROWS + pr;
   if (rho >= p.ag_nq[ai] * p.G) return;  // the whole wave leaves together
   auto prow = [&](int s) { return p.part + (((uint64_t)s * p.nblk + bid) * ROWS + pr) * p.W; };
-  float m_s = -1e30f, l_s = 0.f;
-  if (lane < p.ksplit) {
-    m_s = prow(lane)[D + p.r];
-    l_s = prow(lane)[D + p.r + 1];
+  // Every load is issued here, before the reductions, and unconditionally
+  // (indices clamped into range; the clamped values are weighted by zero or
+  // never read), so the compiler's waits count each group exactly: the
+  // partial rows first, then the first eight rows of B_i's column slice.
+  const float m_l = prow(min(lane, p.ksplit - 1))[D + p.r];
+  const float l_l = prow(min(lane, p.ksplit - 1))[D + p.r + 1];
+  float po[kMaxPrefillSplit][EPL], plr[kMaxPrefillSplit];
+#pragma unroll
+  for (int s = 0; s < kMaxPrefillSplit; ++s) {
+    const float* pp = prow(min(s, p.ksplit - 1));
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) po[s][e] = pp[lane + 64 * e];
+    plr[s] = pp[D + min(lane, p.r - 1)];
   }
+  const int HD = p.Hkv * D;
+  const u16* Bi = p.B + (uint64_t)p.ag_id[ai] * p.r * HD + g * D;
+  u16 b8[8][EPL];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) b8[k][e] = Bi[(uint64_t)min(k, p.r - 1) * HD + lane + 64 * e];
+  const float m_s = lane < p.ksplit ? m_l : -1e30f;
+  const float l_s = lane < p.ksplit ? l_l : 0.f;
   const float M = wave_max(m_s);
   const float w_s = lane < p.ksplit ? __builtin_amdgcn_exp2f(m_s - M) : 0.f;
   const float L = wave_sum(w_s * l_s);
@@ -1652,19 +1671,25 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillMergeParams p
   float acc[EPL], acc_lr = 0.f;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  for (int s = 0; s < p.ksplit; ++s) {
-    const float ws = __shfl(w_s, s);
-    const float* pp = prow(s);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += ws * pp[lane + 64 * e];
-    if (lane < p.r) acc_lr += ws * pp[D + lane];
+  for (int s = 0; s < kMaxPrefillSplit; ++s) {
+    const float ws = __shfl(w_s, s);  // zero past the last range
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += ws * po[s][e];
+    acc_lr += ws * plr[s];  // meaningful in lanes below r
   }
-  const int HD = p.Hkv * D;
-  const u16* Bi = p.B + (uint64_t)p.ag_id[ai] * p.r * HD + g * D;
   float out[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) out[e] = acc[e] * inv;
-  for (int k = 0; k < p.r; ++k) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float lk = __shfl(acc_lr, k) * inv;
+    if (k < p.r) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) out[e] += lk * bf2f(b8[k][e]);
+    }
+  }
+  for (int k = 8; k < p.r; ++k) {
     const float lk = __shfl(acc_lr, k) * inv;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) out[e] += lk * bf2f(Bi[(uint64_t)k * HD + lane + 64 * e]);
@@ -2096,7 +2121,6 @@ int launch_prefill_o(const skv::Geometry& g, const PrefillParams& p, int blocks,
 // workgroups so that the launch fills the CUs; a merge launch combines the
 // partial rows and applies B_i. The partials use the decode scratch (the two
 // kinds of call are ordered on the stream).
-constexpr int kMaxPrefillSplit = 8;
 constexpr int kMinSplitPages = 4;  // pages per workgroup below which a split does not pay
 
 int prefill_split(int nblk, int min_view_pages) {
