@@ -66,12 +66,27 @@ def decode_split_bytes(Hkv, d, r, hidden, prefix, suffixes, n_agents, Hq, bls=Tr
     """Algorithmic bytes the split launch of one fused decode step must move:
     the shared K and V rows once per KV head, the shared low-rank rows (one
     plane, or one per agent), each agent's cached own K/V/low-rank rows, the
-    queries, and the step's appends (new K/V/low-rank rows written, x rows and
-    A read). suffixes are the own lengths before the step."""
+    queries, and the step's low-rank appends (x rows and A read, the rows
+    written). suffixes are the own lengths before the step."""
     shared = 4 * Hkv * d * prefix + 2 * r * (prefix if bls else prefix * n_agents)
     own = sum(s * (4 * Hkv * d + 2 * r) for s in suffixes)
-    append = n_agents * (4 * Hkv * d + 2 * r + 2 * hidden) + 2 * hidden * r
+    append = n_agents * (2 * r + 2 * hidden) + 2 * hidden * r * (1 if bls else n_agents)
     return shared + own + 2 * n_agents * Hq * d + append
+
+
+def decode_step_bytes(Hkv, d, r, hidden, prefix, suffixes, n_agents, Hq, bls=True):
+    """Algorithmic bytes of one fused decode-step launch at one layer: the
+    shared K and V rows once per KV head, the shared low-rank rows (one plane,
+    or one per agent), each agent's cached own K/V/low-rank rows, the queries
+    read and the outputs written, each agent's B_i, and the step's appends (new
+    K/V/low-rank rows written, x rows and A read). suffixes are the own lengths
+    before the step."""
+    shared = 4 * Hkv * d * prefix + 2 * r * (prefix if bls else prefix * n_agents)
+    own = sum(s * (4 * Hkv * d + 2 * r) for s in suffixes)
+    qo = 4 * n_agents * Hq * d
+    b_i = 2 * n_agents * r * Hkv * d
+    append = n_agents * (4 * Hkv * d + 2 * r + 2 * hidden) + 2 * hidden * r * (1 if bls else n_agents)
+    return shared + own + qo + b_i + append
 
 
 def project_flops(Hq, Hkv, d, hidden, r, rows):
@@ -210,18 +225,32 @@ def cpu_baseline(cfg, budget_s=15.0):
     for a in range(N):
         c.crop(a, prefix)
     Bm = rng.standard_normal((N, r, Hkv * d)) * np.sqrt(0.01 / r)
-    steps, t0 = 0, time.perf_counter()
-    while True:
-        k = rng.standard_normal((N, Hkv, d))
-        c.append_agents(0, list(range(N)), [1] * N, k, k, rng.standard_normal((N, hidden)), A)
-        q = rng.standard_normal((N, Hq, d))
-        attention_outputs(c, 0, list(range(N)), [1] * N, q, Bm)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
+
+    def time_decode(budget):
+        steps, t0 = 0, time.perf_counter()
+        while True:
+            k = rng.standard_normal((N, Hkv, d))
+            c.append_agents(0, list(range(N)), [1] * N, k, k, rng.standard_normal((N, hidden)), A)
+            q = rng.standard_normal((N, Hq, d))
+            attention_outputs(c, 0, list(range(N)), [1] * N, q, Bm)
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return steps, el
+
+    steps, el = time_decode(budget_s)
     per_layer = el / steps
     tok_s = N / (per_layer * L)
+    one_core = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            s1, e1 = time_decode(budget_s / 3)
+        one_core = {"value": round(N / (e1 / s1 * L), 4), "unit": "tokens/s", "cores": 1,
+                    "sample": f"{s1} decode steps of 1 layer timed for {e1:.1f} s with BLAS limited to one thread"}
+        steps += s1
+    except Exception as exc:  # threadpoolctl missing: report the all-threads figure only
+        one_core = {"error": str(exc)}
     # the same oracle on a sample of one suffix prefill call (512 own tokens per
     # agent): a few query rows of each agent, scaled to the call's rows
     n_pre = 512
@@ -234,7 +263,12 @@ def cpu_baseline(cfg, budget_s=15.0):
     call_s = (time.perf_counter() - t1) / len(sample) * N * n_pre
     view = prefix + steps + n_pre
     flops = prefill_flops(Hq, d, r, [view] * N, [n_pre] * N)
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count() or 1
     return {"value": round(tok_s, 4), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "nproc": nproc, "one_core": one_core,
             "sample": f"{steps} decode steps of 1 layer (4 agents, fp64, prefix {prefix}) timed for "
                       f"{el:.1f} s; per-layer time x {L} layers",
             "prefill": {"value": round(flops / call_s / 1e12, 6), "unit": "TFLOP/s",
@@ -247,6 +281,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--reps", type=int, default=10,
+                    help="timed repetitions of the K-step loop; value is the median repetition")
     ap.add_argument("--workload", default="llama3-8b-attn-32k", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
@@ -288,7 +324,7 @@ def main():
     G = Hq // Hkv
     total_steps = args.warmup + args.steps
     prefill_n = 512
-    own_max = (args.warmup + 2 * args.steps + (0 if args.no_prefill else prefill_n) + args.mixed * (prefill_n + 1)
+    own_max = (args.warmup + (args.reps + 1) * args.steps + (0 if args.no_prefill else prefill_n) + args.mixed * (prefill_n + 1)
                + (0 if args.no_ttft else prefill_n + 1))
     if private:
         max_pages = N * ((prefix + own_max) // 64 + 2) + 4
@@ -383,18 +419,36 @@ def main():
     B.skv_sync(ctx)
     torch.cuda.synchronize()
 
-    # ---- timed region: K decode steps (no events) -> value ----
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = 1e3 * wall / args.steps
-    value = N * args.steps / wall
+    # ---- timed region: REPS repetitions of K decode steps (no events), each
+    # bracketed by device synchronisation; value = the median repetition ----
+    reps_ms = []
+    for _ in range(args.reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        reps_ms.append(1e3 * (time.perf_counter() - t0))
+    srt = sorted(reps_ms)
+    med_ms = srt[len(srt) // 2] if len(srt) % 2 else 0.5 * (srt[len(srt) // 2 - 1] + srt[len(srt) // 2])
+    ms_per_step = med_ms / args.steps
+    value = N * args.steps / (med_ms / 1e3)
+    spread = {"reps": args.reps, "ms_per_step_min": round(srt[0] / args.steps, 4),
+              "ms_per_step_max": round(srt[-1] / args.steps, 4),
+              "tokens_per_s_min": round(N * args.steps / (srt[-1] / 1e3), 2),
+              "tokens_per_s_max": round(N * args.steps / (srt[0] / 1e3), 2)}
+    # algorithmic bytes of one step over all layers (at the views of the timed
+    # repetitions' middle step) against the median step time
+    mid_S = S[0] - (args.reps * args.steps) // 2
+    step_bytes = L * decode_step_bytes(Hkv, d, r, hidden, base0, [mid_S] * N, N, Hq, bls=mode == 1)
+    step_gbs = step_bytes / (ms_per_step / 1e3) / 1e9
+    step_roofline = {"bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(step_gbs / HBM_PEAK_GBS, 4), "measured_peak": round(stream_gbs, 1),
+                     "frac_of_measured": round(step_gbs / stream_gbs, 4),
+                     "algorithmic_bytes_per_step": int(step_bytes), "launches_per_step": 2 * L}
 
     # ---- second timed region: the same steps with HIP events recorded by the
-    # dispatch of each split launch on the library's stream -> roofline ----
+    # dispatch of each decode launch on the library's stream -> roofline ----
     suffix_hist = []
     times = {}
     if not args.no_events:
@@ -440,8 +494,10 @@ def main():
             B.skv_attn_prefill(ctx, l, agents, [base0] * N, [Ssuf] * N, [prefill_n] * N, qp, Bw, op)
         pt = B.skv_collect_timing(ctx)
         B.skv_set_timing(ctx, False)
-        pms, pn = pt["prefill"]
-        pn = L  # one call per layer; a call whose key ranges are split also launches a merge
+        # one call per layer: the prefill launch, plus a merge launch when its key
+        # ranges are split
+        pms = pt["prefill"][0]
+        pn = L
         fl = prefill_flops(Hq, d, r, [base0 + Ssuf] * N, [prefill_n] * N)
         tf = fl / (pms / 1e3 / pn) / 1e12
         prefill = {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -521,7 +577,7 @@ def main():
 
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "timing": spread,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "layers": L, "q_heads": Hq, "kv_heads": Hkv,
@@ -531,6 +587,7 @@ def main():
                    "decode_tokens_per_step": N, "global_batch": N, "seq_len": prefix,
                    "parallelism": "single-gpu"},
         "roofline": roofline,
+        "step_roofline": step_roofline,
         "kernels": per_kernel,
         "prefill": prefill,
         "memory": memory,

@@ -269,8 +269,9 @@ int skv_get_counters(const skv_ctx* ctx, skv_counters* out);
 
 /* Kernel timing with HIP events recorded on the context stream around each
  * launch, while enabled. Kinds: 0 append K/V, 1 append low-rank, 2 decode
- * attention (split pass), 3 decode merge + B, 4 prefill attention, 5 front-end
- * projection (skv_project_append). */
+ * attention (split pass), 3 decode merge + B_i, 4 prefill attention (and the
+ * merge launch of a prefill whose key ranges are split), 5 front-end
+ * projection (skv_project_append) and weight packing. */
 #define SKV_KERNEL_KINDS 6
 typedef struct skv_kernel_times {
   double ms[SKV_KERNEL_KINDS];

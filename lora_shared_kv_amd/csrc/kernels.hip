@@ -43,6 +43,7 @@
 #include <vector>
 
 #include "backend.h"
+#include "plan.h"
 
 namespace skv {
 // Written by the probe kernels only on an impossible value; external linkage,
@@ -58,13 +59,13 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef uint16_t u16;
 
-constexpr int kPage = 64;           // rows per page in the GPU build
-constexpr int kMaxDecodeRows = 64;  // query rows (agents x G) per decode launch
-constexpr int kMaxItems = 2048;     // decode work items per launch (partials capacity)
-constexpr int kMaxMergeSlots = 1024;
-constexpr int kMaxViewPages = 4096;  // prefill view length cap: 262144 tokens
-constexpr int kMaxItemChunks = 512;  // 32-key chunks per decode item
-constexpr int kCUs = 256;
+constexpr int kPage = skv::kPlanPage;  // rows per page in the GPU build
+using skv::kMaxDecodeRows;
+using skv::kMaxItems;
+using skv::kMaxMergeSlots;
+using skv::kMaxViewPages;
+using skv::kMaxItemChunks;
+constexpr int kCUs = skv::kPlanCUs;
 
 char g_err[256] = "";
 void set_err(const char* what, hipError_t e) {
@@ -912,10 +913,13 @@ struct MergeParams {
 // w_s = 2^(m_s - M) / sum_s 2^(m_s - M) l_s, o = sum_s w_s o_s and
 // o_lr = sum_s w_s o_lr,s (a fused step adds the new token's own term);
 // then applies B_i once: o[d] += sum_k o_lr[k] B_i[k][g*D + d], in bf16.
-// Every global load the row needs is issued before the first reduction, so
-// the kernel waits on memory about once.
+// Every global load of the row (partial rows, the B_i slice, the new token)
+// is issued up front and unconditionally, with indices past the end clamped
+// and their terms dropped, so the row waits on memory once; B_i is staged in
+// LDS for the final product.
 constexpr int kMergeVec = 8;  // slots per thread held in registers
 
+template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
   extern __shared__ __attribute__((aligned(16))) char s_app[];  // append blocks' staging
   if ((int)blockIdx.x >= p.n_rows) {
@@ -927,103 +931,110 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
   __shared__ float s_w[kMaxMergeSlots];
   __shared__ f32x4 s_red[8][40];
   __shared__ float s_v[128 + 32];
-  __shared__ float s_m[4], s_l[4];
-  __shared__ float s_new;
+  __shared__ float s_sm[16];  // maxima [4], sums [4], new score
+  __shared__ u32x4 s_b[32 * 128 / 8];  // B_i slice [r][D] bf16
   const int row_id = blockIdx.x;
   const int hh = row_id % p.G;
   const int g = (row_id / p.G) % p.Hkv;
   const int a = row_id / (p.G * p.Hkv);
   const int rho = a * p.G + hh;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int n_slots = p.items_per_head;
-  const int E = p.D + p.r;
-  auto slot_row = [&](int s) {
-    return p.part + ((uint64_t)(g * p.items_per_head + s) * p.R + rho) * p.W;
-  };
-  // --- issue loads: per-slot (m, l), this thread's element quads, the new token
-  float m_s = -1e30f, l_s = 0.f;
-  if (threadIdx.x < n_slots) {
-    m_s = slot_row(threadIdx.x)[E];
-    l_s = slot_row(threadIdx.x)[E + 1];
-  }
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int I = p.items_per_head, W = p.W, r = p.r;
+  const int E = D + r;
+  auto slot_row = [&](int s) { return p.part + ((uint64_t)(g * I + s) * p.R + rho) * W; };
+  // --- loads: per-slot (m, l), this thread's element quads, B_i, the new token
+  const int ts = max(min(t, I - 1), 0);
+  float m_ld = 0.f, l_ld = 0.f;
   const int NQ = E / 4;
   const int NG = min(8, (int)blockDim.x / NQ);
-  const int qd = threadIdx.x % NQ, sg = threadIdx.x / NQ;
-  const bool quad_thread = sg < NG;
+  const int qd = t % NQ, sg = min(t / NQ, NG - 1);
+  const bool quad_thread = t < NQ * NG;
   f32x4 vals[kMergeVec];
-  int n_mine = 0;
-  if (quad_thread) {
+  if (I > 0) {  // uniform: no slots when nothing was cached before a fused step
+    m_ld = slot_row(ts)[E];
+    l_ld = slot_row(ts)[E + 1];
 #pragma unroll
-    for (int i = 0; i < kMergeVec; ++i) {
-      const int s = sg + i * NG;
-      if (s < n_slots) {
-        vals[i] = *reinterpret_cast<const f32x4*>(slot_row(s) + 4 * qd);
-        n_mine = i + 1;
-      }
-    }
+    for (int i = 0; i < kMergeVec; ++i)
+      vals[i] = *reinterpret_cast<const f32x4*>(slot_row(min(sg + i * NG, I - 1)) + 4 * qd);
   }
-  float dot = 0.f;
-  if (p.step && w == 0) {
-    const u16* qr = p.q + ((uint64_t)a * p.Hq + g * p.G + hh) * p.D;
-    const u16* kr = p.k_new + ((uint64_t)a * p.Hkv + g) * p.D;
-    for (int d = lane; d < p.D; d += 64) dot += bf2f(qr[d]) * bf2f(kr[d]);
+  const int HD = p.Hkv * D;
+  constexpr int BV = D / 8;  // 16-byte vectors per B_i row slice
+  const u16* bsl = p.B + (uint64_t)p.ag_id[a] * r * HD + g * D;
+  u32x4 bvec[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int v = min(t + 256 * i, r * BV - 1);
+    bvec[i] = *reinterpret_cast<const u32x4*>(bsl + (uint64_t)(v / BV) * HD + 8 * (v % BV));
   }
-  float nv = 0.f;  // the new token's value for element threadIdx.x (v row, then low-rank row)
-  if (p.step && threadIdx.x < E) {
-    const int e = threadIdx.x;
-    nv = e < p.D ? bf2f(p.v_new[((uint64_t)a * p.Hkv + g) * p.D + e])
-         : !p.new_lr_on[a] ? 0.f
-                           : bf2f(p.LRT[(uint64_t)p.plane[a] * p.lr_plane + (uint64_t)p.new_page[a] * p.r * kPage +
-                                        (e - p.D) * kPage + p.new_slot[a]]);
+  float dot = 0.f, nv = 0.f;
+  if (p.step) {
+    // the new token's score q . k_new (two elements per lane of wave 0) and its
+    // value element t (its v row, then its low-rank row)
+    const u16* qr = p.q + ((uint64_t)a * p.Hq + g * p.G + hh) * D;
+    const u16* kr = p.k_new + ((uint64_t)a * p.Hkv + g) * D;
+    const int dl = (2 * lane) % D;
+    const uint32_t qw = *reinterpret_cast<const uint32_t*>(qr + dl), kw = *reinterpret_cast<const uint32_t*>(kr + dl);
+    const float vv = bf2f(p.v_new[((uint64_t)a * p.Hkv + g) * D + min(t, D - 1)]);
+    const float lv = bf2f(p.LRT[(uint64_t)p.plane[a] * p.lr_plane + (uint64_t)p.new_page[a] * r * kPage +
+                                min(max(t - D, 0), r - 1) * kPage + p.new_slot[a]]);
+    if (2 * lane < D)
+      dot = __uint_as_float(qw << 16) * __uint_as_float(kw << 16) +
+            __uint_as_float(qw & 0xffff0000u) * __uint_as_float(kw & 0xffff0000u);
+    nv = t < D ? vv : (t < E && p.new_lr_on[a] ? lv : 0.f);
   }
   // --- softmax statistics
+  const float m_s = t < I ? m_ld : -1e30f, l_s = t < I ? l_ld : 0.f;
   float M = wave_max(m_s);
   if (p.step && w == 0) {
     dot = wave_sum(dot);
-    if (lane == 0) s_new = dot * p.scale_log2;
+    if (lane == 0) s_sm[8] = dot * p.scale_log2;
   }
-  if (lane == 0) s_m[w] = M;
+  if (lane == 0) s_sm[w] = M;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    if (t + 256 * i < r * BV) s_b[t + 256 * i] = bvec[i];
   __syncthreads();
-  const float m_new = p.step ? s_new : -1e30f;
-  M = fmaxf(fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3])), m_new);
+  const float m_new = p.step ? s_sm[8] : -1e30f;
+  M = fmaxf(fmaxf(fmaxf(s_sm[0], s_sm[1]), fmaxf(s_sm[2], s_sm[3])), m_new);
   // slots beyond the first blockDim.x are folded in below through s_w
-  float e_s = threadIdx.x < n_slots ? __builtin_amdgcn_exp2f(m_s - M) : 0.f;
-  if (threadIdx.x < n_slots) s_w[threadIdx.x] = e_s;
+  const float e_s = t < I ? __builtin_amdgcn_exp2f(m_s - M) : 0.f;
+  if (t < I) s_w[t] = e_s;
   float L = e_s * l_s;
-  for (int s = threadIdx.x + blockDim.x; s < n_slots; s += blockDim.x) {
+  for (int s = t + blockDim.x; s < I; s += blockDim.x) {
     const float e = __builtin_amdgcn_exp2f(slot_row(s)[E] - M);
     s_w[s] = e;
     L += e * slot_row(s)[E + 1];
   }
   L = wave_sum(L);
-  if (lane == 0) s_l[w] = L;
+  if (lane == 0) s_sm[4 + w] = L;
   __syncthreads();
   const float e_new = p.step ? __builtin_amdgcn_exp2f(m_new - M) : 0.f;
-  const float inv = 1.f / (s_l[0] + s_l[1] + s_l[2] + s_l[3] + e_new);
+  const float inv = 1.f / (s_sm[4] + s_sm[5] + s_sm[6] + s_sm[7] + e_new);
   // --- weighted sums: element quads x slot groups
   if (quad_thread) {
     f32x4 acc = {0, 0, 0, 0};
+    if (I > 0) {
 #pragma unroll
-    for (int i = 0; i < kMergeVec; ++i)
-      if (i < n_mine) acc += s_w[sg + i * NG] * vals[i];
-    for (int s = sg + kMergeVec * NG; s < n_slots; s += NG)
-      acc += s_w[s] * *reinterpret_cast<const f32x4*>(slot_row(s) + 4 * qd);
+      for (int i = 0; i < kMergeVec; ++i) {
+        const int s = sg + i * NG;
+        acc += (s < I ? s_w[s] : 0.f) * vals[i];
+      }
+    }
+    for (int s = sg + kMergeVec * NG; s < I; s += NG) acc += s_w[s] * *reinterpret_cast<const f32x4*>(slot_row(s) + 4 * qd);
     s_red[sg][qd] = acc;
   }
   __syncthreads();
-  if (threadIdx.x < E) {
-    const int e = threadIdx.x;
+  if (t < E) {
     float acc = 0.f;
-    for (int gg = 0; gg < NG; ++gg) acc += s_red[gg][e / 4][e % 4];
-    s_v[e] = (acc + e_new * nv) * inv;
+    for (int gg = 0; gg < NG; ++gg) acc += s_red[gg][t / 4][t % 4];
+    s_v[t] = (acc + e_new * nv) * inv;
   }
   __syncthreads();
-  const int HD = p.Hkv * p.D;
-  for (int d = threadIdx.x; d < p.D; d += blockDim.x) {
-    float out = s_v[d];
-    const u16* bcol = p.B + (uint64_t)p.ag_id[a] * p.r * HD + g * p.D + d;
-    for (int k = 0; k < p.r; ++k) out += s_v[p.D + k] * bf2f(bcol[(uint64_t)k * HD]);
-    p.o[((uint64_t)a * p.Hq + g * p.G + hh) * p.D + d] = f2bf(out);
+  if (t < D) {
+    const u16* bl = reinterpret_cast<const u16*>(s_b);
+    float out = s_v[t];
+    for (int k = 0; k < r; ++k) out += s_v[D + k] * bf2f(bl[k * D + t]);
+    p.o[((uint64_t)a * p.Hq + g * p.G + hh) * D + t] = f2bf(out);
   }
 }
 
@@ -2067,19 +2078,7 @@ int launch(const skv::Geometry& g, int kind, Kernel kernel, dim3 grid, size_t ld
   return SKV_OK;
 }
 
-int decode_group_limit(const skv::Geometry& g) {
-  // agents per decode launch: rows <= 64, stacked low-rank rows <= 128,
-  // and (row blocks x low-rank blocks) <= 8
-  for (int ng = std::min(g.N, kMaxDecodeRows / g.G); ng >= 1; --ng) {
-    int planes = g.mode == SKV_BASE_SHARED ? ng : 1;
-    int rb = (ng * g.G + 15) / 16;
-    rb = rb <= 1 ? 1 : (rb <= 2 ? 2 : 4);
-    int mb = (planes * g.r + 15) / 16;
-    mb = mb <= 1 ? 1 : (mb <= 2 ? 2 : (mb <= 4 ? 4 : 8));
-    if (planes * g.r <= 128 && rb * mb <= 8) return ng;
-  }
-  return 0;
-}
+int group_limit(const skv::Geometry& g) { return skv::decode_group_limit(g.N, g.G, g.mode, g.r); }
 
 int w_of(const skv::Geometry& g) { return g.D + g.r + 4; }
 
@@ -2151,7 +2150,7 @@ namespace skv {
 int dev_check(const Geometry& g) {
   if (g.ps != kPage) return SKV_ERR_UNSUPPORTED;
   if (g.G > kMaxDecodeRows) return SKV_ERR_UNSUPPORTED;
-  if (decode_group_limit(g) < 1) return SKV_ERR_UNSUPPORTED;
+  if (group_limit(g) < 1) return SKV_ERR_UNSUPPORTED;
   return SKV_OK;
 }
 
@@ -2262,7 +2261,7 @@ int dev_project(const Geometry& g, const ProjectJob& job) {
 // fused decode step) each group's split launch also writes the group's new
 // rows and the merge adds the new tokens.
 static int decode_impl(const Geometry& g, const AttnJob& job, const AppendJob* app) {
-  const int ng = decode_group_limit(g);
+  const int ng = group_limit(g);
   hipStream_t st = (hipStream_t)g.stream;
   const int W = w_of(g);
   float* part = (float*)(g.arena + g.scratch_off);
@@ -2349,15 +2348,9 @@ static int decode_impl(const Geometry& g, const AttnJob& job, const AppendJob* a
     p.seg_off[0] = p.shared_len;
     for (int i = 0; i < n; ++i) p.seg_off[i + 1] = p.seg_off[i] + (p.ag_S[i] + 31) / 32 * 32;
     const int chunks = p.seg_off[n] / 32;
-    // items: as many per KV head as leave one CU per workgroup next to the
-    // append blocks, each a balanced run of whole chunks (0 items when nothing
-    // is cached yet)
-    int items_per_head = 0;
-    if (chunks > 0) {
-      items_per_head = std::min(chunks, std::max(1, (kCUs - p.n_app) / g.Hkv));
-      items_per_head = std::max(items_per_head, (chunks + kMaxItemChunks - 1) / kMaxItemChunks);
-    }
-    if ((uint64_t)items_per_head * g.Hkv > (uint64_t)kMaxItems || items_per_head > kMaxMergeSlots) {
+    // items per KV head: the same plan the runtime has checked the call against
+    const int items_per_head = skv::decode_items_per_head(chunks, p.n_app, g.Hkv);
+    if (items_per_head < 0) {
       snprintf(g_err, sizeof g_err, "decode view too long for the split plan (%d keys)", p.seg_off[n]);
       return SKV_ERR_UNSUPPORTED;
     }
@@ -2407,8 +2400,9 @@ static int decode_impl(const Geometry& g, const AttnJob& job, const AppendJob* a
       mp.n_app = n_kv_app;
     }
     mp.n_rows = n * g.Hkv * g.G;
-    rc = launch(g, 3, decode_merge_kernel, dim3(mp.n_rows + mp.n_app),
-                mp.n_app ? (size_t)64 * (128 + 8) * 2 : 0, mp, "decode_merge_kernel");
+    const size_t mlds = mp.n_app ? (size_t)64 * (128 + 8) * 2 : 0;
+    rc = g.D == 128 ? launch(g, 3, decode_merge_kernel<128>, dim3(mp.n_rows + mp.n_app), mlds, mp, "decode_merge_kernel")
+                    : launch(g, 3, decode_merge_kernel<64>, dim3(mp.n_rows + mp.n_app), mlds, mp, "decode_merge_kernel");
     if (rc != SKV_OK) return rc;
   }
   return SKV_OK;

@@ -21,6 +21,7 @@
 #include <vector>
 
 #include "backend.h"
+#include "plan.h"
 
 namespace {
 
@@ -466,6 +467,8 @@ int skv_attn_prefill(skv_ctx* c, int layer, int n, const int* agents, const int*
   AttnJob job;
   int rc = validate_attend(c, layer, n, agents, base_len, suffix_len, n_q, q, B, o, job);
   if (rc != SKV_OK) return rc;
+  char msg[256];
+  if ((rc = skv::plan_check_prefill(job, msg, sizeof msg)) != SKV_OK) return c->fail(rc, "%s", msg);
   rc = skv::dev_attn_prefill(c->g, job);
   if (rc != SKV_OK) return c->fail(rc, "device prefill failed: %s", skv::dev_last_error());
   return SKV_OK;
@@ -477,6 +480,8 @@ int skv_attn_decode(skv_ctx* c, int layer, int n, const int* agents, const int* 
   AttnJob job;
   int rc = validate_attend(c, layer, n, agents, base_len, suffix_len, nullptr, q, B, o, job);
   if (rc != SKV_OK) return rc;
+  char msg[256];
+  if ((rc = skv::plan_check_decode(c->g, job, false, msg, sizeof msg)) != SKV_OK) return c->fail(rc, "%s", msg);
   rc = skv::dev_attn_decode(c->g, job);
   if (rc != SKV_OK) return c->fail(rc, "device decode failed: %s", skv::dev_last_error());
   return SKV_OK;
@@ -521,6 +526,9 @@ int skv_decode_step(skv_ctx* c, int layer, int n, const int* agents, const int* 
   }
   if (need > (int)l.free.size())
     return c->fail(SKV_ERR_OOM, "layer %d: %d pages needed, %d free", layer, need, (int)l.free.size());
+  char msg[256];
+  int rc = skv::plan_check_decode(g, job, true, msg, sizeof msg);
+  if (rc != SKV_OK) return c->fail(rc, "%s", msg);
   std::vector<std::vector<int32_t>> tables(n);
   std::vector<int32_t> taken;
   for (int i = 0; i < n; ++i) {
@@ -561,7 +569,7 @@ int skv_decode_step(skv_ctx* c, int layer, int n, const int* agents, const int* 
   job.q = q;
   job.B = B;
   job.o = o;
-  int rc = skv::dev_decode_step(g, job, app);
+  rc = skv::dev_decode_step(g, job, app);
   if (rc != SKV_OK) {
     for (int32_t p : taken) l.free.insert(p);
     return c->fail(rc, "device decode step failed: %s", skv::dev_last_error());
