@@ -24,7 +24,9 @@
  *
  * Conventions
  *   - All tensors are bf16 (passed as uint16_t bit patterns), row-major and
- *     contiguous, and live in DEVICE memory: k, v, x, A, B, q, o.
+ *     contiguous, and live in DEVICE memory: k, v, x, A, B, q, o. Each starts
+ *     at a 16-byte-aligned address (the kernels use 16-byte vector accesses);
+ *     a misaligned pointer is rejected with SKV_ERR_ARG.
  *   - Small integer arrays (agents, lengths, counts) live in HOST memory.
  *   - Hq = n_q_heads, Hkv = n_kv_heads, G = Hq / Hkv, d = head_dim,
  *     r = rank, N = n_agents. Query head h reads KV head floor(h / G).

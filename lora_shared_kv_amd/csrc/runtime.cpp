@@ -16,6 +16,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <set>
 #include <string>
 #include <vector>
@@ -39,6 +40,13 @@ struct Layer {
 };
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Device tensors are read and written with 16-byte vector accesses.
+bool aligned16(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if ((uintptr_t)p & 15) return false;
+  return true;
+}
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 bool valid_config(const skv_config* c) {
@@ -335,6 +343,7 @@ int skv_append_base(skv_ctx* c, int layer, int seq, int n, const skv_bf16* k, co
   if (n < 0) return c->fail(SKV_ERR_ARG, "negative row count");
   if (n == 0) return SKV_OK;
   if (!k || !v) return c->fail(SKV_ERR_ARG, "null k or v");
+  if (!aligned16({k, v})) return c->fail(SKV_ERR_ARG, "k and v must be 16-byte aligned");
   Layer& l = c->layers[layer];
   const int slot = skv_ctx::slot_of(seq);
   const int cur = l.len[slot];
@@ -382,6 +391,7 @@ int skv_append_lowrank(skv_ctx* c, int layer, int seq, int plane, int n, const s
   }
   if (n < 0) return c->fail(SKV_ERR_ARG, "negative row count");
   if (x && !A) return c->fail(SKV_ERR_ARG, "x given without A");
+  if (!aligned16({x, x ? A : nullptr})) return c->fail(SKV_ERR_ARG, "x and A must be 16-byte aligned");
   if (n == 0) return SKV_OK;
   Layer& l = c->layers[layer];
   const int slot = skv_ctx::slot_of(seq);
@@ -411,6 +421,8 @@ int skv_append_agents(skv_ctx* c, int layer, int n, const int* agents, const int
   int rc = check_agent_rows(c, layer, n, agents, counts, &total);
   if (rc != SKV_OK || total == 0) return rc;
   if (!k || !v) return c->fail(SKV_ERR_ARG, "null k or v");
+  if (!aligned16({k, v, x, x ? A : nullptr}))
+    return c->fail(SKV_ERR_ARG, "k, v, x and A must be 16-byte aligned");
   AgentRows ar;
   rc = plan_agent_rows(c, layer, n, agents, counts, k, v, x, A, ar);
   if (rc != SKV_OK) return rc;
@@ -426,6 +438,7 @@ static int validate_attend(skv_ctx* c, int layer, int n, const int* agents, cons
   if (n < 1 || n > g.N) return c->fail(SKV_ERR_ARG, "agent count %d", n);
   if (!agents || !base_len || !suffix_len || !q || !B || !o)
     return c->fail(SKV_ERR_ARG, "null argument");
+  if (!aligned16({q, B, o})) return c->fail(SKV_ERR_ARG, "q, B and o must be 16-byte aligned");
   const Layer& l = c->layers[layer];
   uint32_t seen = 0;
   for (int i = 0; i < n; ++i) {
@@ -498,6 +511,8 @@ int skv_decode_step(skv_ctx* c, int layer, int n, const int* agents, const int* 
   if (!agents || !base_len || !suffix_len || !k || !v || !q || !B || !o)
     return c->fail(SKV_ERR_ARG, "null argument");
   if (x && !A) return c->fail(SKV_ERR_ARG, "x given without A");
+  if (!aligned16({k, v, x, x ? A : nullptr, q, B, o}))
+    return c->fail(SKV_ERR_ARG, "device pointers must be 16-byte aligned");
   Layer& l = c->layers[layer];
   uint32_t seen = 0;
   for (int i = 0; i < n; ++i) {
@@ -589,6 +604,7 @@ int skv_decode_step(skv_ctx* c, int layer, int n, const int* agents, const int* 
 int skv_pack_qkv(skv_ctx* c, const skv_bf16* w_qkv, skv_bf16* w_packed) {
   if (!c) return SKV_ERR_ARG;
   if (!w_qkv || !w_packed) return c->fail(SKV_ERR_ARG, "null w_qkv or w_packed");
+  if (!aligned16({w_qkv, w_packed})) return c->fail(SKV_ERR_ARG, "w_qkv and w_packed must be 16-byte aligned");
   const Geometry& g = c->g;
   const uint64_t bytes = 2ull * (g.Hq + 2 * g.Hkv) * g.D * g.hidden;
   const uintptr_t a = (uintptr_t)w_qkv, b = (uintptr_t)w_packed;
@@ -606,6 +622,7 @@ int skv_project_append(skv_ctx* c, int layer, int n, const int* agents, const in
   int rc = check_agent_rows(c, layer, n, agents, counts, &total);
   if (rc != SKV_OK || total == 0) return rc;
   if (!x || !w_packed || !q_out) return c->fail(SKV_ERR_ARG, "null x, w_packed or q_out");
+  if (!aligned16({x, w_packed, A, q_out})) return c->fail(SKV_ERR_ARG, "device pointers must be 16-byte aligned");
   if (!(rope_theta == 0.f || (rope_theta > 1.f && rope_theta < 1e30f)))
     return c->fail(SKV_ERR_ARG, "rotary base %g (0 or above 1)", (double)rope_theta);
   AgentRows ar;

@@ -1,0 +1,126 @@
+"""Every attention call is checked against the GPU launch plan on the host, before
+anything is enqueued: a call past a plan limit returns UNSUPPORTED and leaves the
+cache exactly as it was (no launch, no page taken, no length changed).
+
+Runs on libskv_host.so (the host runtime with the null device backend), which
+applies the same plan checks as the GPU build. The limits (plan.h):
+  decode: per launch, items per KV head <= min(2048 / Hkv, 1024), each item at
+    most 512 chunks of 32 keys, so a KV head's flattened view (shared prefix up
+    to the largest b_i, then every own suffix, each padded to 32 keys) holds at
+    most 32 * 512 * min(2048 / Hkv, 1024) keys;
+  prefill: a view spans at most 4096 pages of 64 rows (shared and own pages
+    counted separately).
+"""
+import pytest
+
+from lora_shared_kv_amd import skv as B
+
+FAKE = 0x100000  # a non-null "device" address; the null backend never dereferences it
+
+# 64 KV heads: at most 32 items per head, 32 * 512 * 32 = 524,288 keys per launch
+CFG = dict(n_layers=1, n_q_heads=64, n_kv_heads=64, head_dim=64, hidden=64, rank=4, n_agents=2,
+           mode=0, page_size=64, max_pages=8200)
+DECODE_KEYS = 32 * 512 * (2048 // 64)
+PREFILL_ROWS = 4096 * 64
+
+
+def make(shared_rows):
+    n = B.skv_arena_bytes(CFG, "host")
+    ctx = B.skv_create(CFG, (1 << 24, n), None, "host")
+    B.skv_append_base(ctx, 0, -1, FAKE, FAKE, n=shared_rows)
+    for plane in range(2):
+        B.skv_append_lowrank(ctx, 0, -1, plane, shared_rows, None, None)
+    return ctx
+
+
+def state(ctx):
+    return (B.skv_get_lens(ctx, 0), B.skv_get_counters(ctx),
+            [B.skv_get_pages(ctx, 0, s) for s in (-1, 0, 1)])
+
+
+def expect_unsupported(ctx, fn, *args):
+    before = state(ctx)
+    with pytest.raises(B.SkvError) as e:
+        fn(ctx, *args)
+    assert e.value.code == "UNSUPPORTED", e.value
+    assert state(ctx) == before
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    return make(DECODE_KEYS + 64)
+
+
+def test_decode_at_and_past_the_view_limit(ctx):
+    B.skv_crop(ctx, 0, DECODE_KEYS)
+    n0 = B.skv_get_counters(ctx)["launches"]
+    B.skv_attn_decode(ctx, 0, [0], [DECODE_KEYS], [0], FAKE, FAKE, FAKE)
+    assert B.skv_get_counters(ctx)["launches"] > n0
+    B.skv_crop(ctx, 0, 0)
+    B.skv_crop(ctx, 0, DECODE_KEYS + 1)  # one key past: one more chunk
+    expect_unsupported(ctx, B.skv_attn_decode, 0, [0], [DECODE_KEYS + 1], [0], FAKE, FAKE, FAKE)
+
+
+def test_fused_step_past_the_view_limit_takes_no_page(ctx):
+    B.skv_crop(ctx, 0, 0)
+    B.skv_crop(ctx, 0, DECODE_KEYS + 32)
+    expect_unsupported(ctx, B.skv_decode_step, 0, [0], [DECODE_KEYS + 32], [0], FAKE, FAKE, FAKE, FAKE, FAKE,
+                       FAKE, FAKE)
+    # at the limit the step runs, appends the agent's row and takes its page
+    B.skv_crop(ctx, 0, 0)
+    B.skv_crop(ctx, 0, DECODE_KEYS)
+    B.skv_decode_step(ctx, 0, [0], [DECODE_KEYS], [0], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert B.skv_get_lens(ctx, 0)["S"][0] == 1
+    B.skv_crop(ctx, 0, DECODE_KEYS)
+
+
+def test_decode_limit_counts_every_agent_of_a_launch(ctx):
+    # two agents share one launch: the shared prefix once, plus each own suffix
+    B.skv_crop(ctx, 0, 0)
+    B.skv_crop(ctx, 1, 0)
+    B.skv_crop(ctx, 0, DECODE_KEYS - 32)
+    B.skv_crop(ctx, 1, DECODE_KEYS - 64)
+    B.skv_append_agents(ctx, 0, [0, 1], [32, 1], FAKE, FAKE, None, None)
+    # flattened: DECODE_KEYS - 32 shared keys + 32 + 32 (padded) own keys: one chunk too many
+    expect_unsupported(ctx, B.skv_attn_decode, 0, [0, 1], [DECODE_KEYS - 32, DECODE_KEYS - 64], [32, 1], FAKE,
+                       FAKE, FAKE)
+    # each agent alone fits
+    B.skv_attn_decode(ctx, 0, [0], [DECODE_KEYS - 32], [32], FAKE, FAKE, FAKE)
+    B.skv_attn_decode(ctx, 0, [1], [DECODE_KEYS - 64], [1], FAKE, FAKE, FAKE)
+    B.skv_crop(ctx, 0, 0)
+    B.skv_crop(ctx, 1, 0)
+
+
+def test_prefill_at_and_past_the_view_limit(ctx):
+    B.skv_crop(ctx, 0, 0)
+    B.skv_crop(ctx, 0, PREFILL_ROWS)
+    B.skv_attn_prefill(ctx, 0, [0], [PREFILL_ROWS], [0], [16], FAKE, FAKE, FAKE)
+    B.skv_crop(ctx, 0, 0)
+    B.skv_crop(ctx, 0, PREFILL_ROWS + 1)
+    expect_unsupported(ctx, B.skv_attn_prefill, 0, [0], [PREFILL_ROWS + 1], [0], [16], FAKE, FAKE, FAKE)
+    # own pages count separately from shared pages
+    B.skv_crop(ctx, 0, 0)
+    B.skv_crop(ctx, 0, PREFILL_ROWS - 10)
+    B.skv_append_agents(ctx, 0, [0], [20], FAKE, FAKE, None, None)
+    expect_unsupported(ctx, B.skv_attn_prefill, 0, [0], [PREFILL_ROWS - 10], [20], [16], FAKE, FAKE, FAKE)
+    B.skv_crop(ctx, 0, 0)
+
+
+def test_misaligned_device_pointers_are_rejected(ctx):
+    # the kernels use 16-byte vector accesses on every device tensor
+    B.skv_crop(ctx, 0, 0)
+    B.skv_crop(ctx, 0, 1000)
+    before = state(ctx)
+    calls = [
+        (B.skv_append_base, (0, 0, FAKE + 2, FAKE), dict(n=4)),
+        (B.skv_append_agents, (0, [0], [4], FAKE, FAKE + 8, None, None), {}),
+        (B.skv_attn_decode, (0, [0], [1000], [0], FAKE, FAKE + 4, FAKE), {}),
+        (B.skv_attn_prefill, (0, [0], [1000], [0], [4], FAKE + 2, FAKE, FAKE), {}),
+        (B.skv_decode_step, (0, [0], [1000], [0], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2), {}),
+    ]
+    for fn, args, kw in calls:
+        with pytest.raises(B.SkvError) as e:
+            fn(ctx, *args, **kw)
+        assert e.value.code == "ARG", (fn.__name__, e.value)
+        assert state(ctx) == before
+    B.skv_crop(ctx, 0, 0)
