@@ -213,6 +213,21 @@ int skv_decode_step(skv_ctx* ctx, int layer, int n, const int* agents, const int
                     const skv_bf16* x, const skv_bf16* A, const skv_bf16* q, const skv_bf16* B,
                     skv_bf16* o);
 
+/* skv_decode_step for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same arguments, results and errors, but the split pass's partial rows go to
+ * the library's static device scratch instead of the arena. The scratch is one
+ * array of 16 MiB per GPU the library runs on, held until the process ends;
+ * this call allocates nothing and records no timing events. Every call on one
+ * GPU shares that array: calls on the same stream are ordered, calls that
+ * overlap on one GPU (other streams, other contexts) race. Extra error:
+ * UNSUPPORTED when a launch's partial rows (split items x agents x G rows x
+ * (d + r + 4) fp32 values) exceed 16 MiB; nothing is appended then. */
+int skv_decode_step_static(skv_ctx* ctx, int layer, int n, const int* agents, const int* base_len,
+                           const int* suffix_len, const skv_bf16* k, const skv_bf16* v,
+                           const skv_bf16* x, const skv_bf16* A, const skv_bf16* q,
+                           const skv_bf16* B, skv_bf16* o);
+
 /* Adapter activation offset of one agent (RoleKV, "What it does": an
  * activated adapter switches on after the role's header, and everything
  * before it is processed with the base weights; "Challenges we ran into": the

@@ -96,6 +96,10 @@ int dev_pack_qkv(const Geometry& g, const uint16_t* w, uint16_t* out);
 // Fused decode step: job holds lengths before the step; app appends one row
 // per agent (in the same order as job.ag).
 int dev_decode_step(const Geometry& g, const AttnJob& job, const AppendJob& app);
+// The same with the partial rows in the library's static device scratch
+// (kStaticScratchBytes, one array per device): no device memory is allocated,
+// no timing events are recorded.
+int dev_decode_step_static(const Geometry& g, const AttnJob& job, const AppendJob& app);
 int dev_attn_prefill(const Geometry& g, const AttnJob& job);
 int dev_sync(const Geometry& g);
 int dev_set_timing(Geometry& g, int mask);

@@ -40,6 +40,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "backend.h"
@@ -50,6 +51,12 @@ namespace skv {
 // so the compiler must keep the work that feeds it.
 __device__ unsigned int probe_sink[4];
 }  // namespace skv
+
+// Static device scratch of skv_decode_step_static (callers that cannot
+// allocate): the decode partial rows, kStaticScratchBytes, one copy per device
+// for the life of the process. Host code never passes this name to a kernel:
+// it takes the array's device address per device with hipGetSymbolAddress.
+static __device__ __align__(256) float scratch[skv::kStaticScratchBytes / sizeof(float)];
 
 namespace {
 
@@ -2032,6 +2039,7 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters) {
 
 struct DevState {
   int timing = 0;  // bit mask of kernel kinds to time
+  float* scratch_static = nullptr;  // device address of `scratch` on this context's device
   std::vector<hipEvent_t> pool;
   struct Rec {
     int kind;
@@ -2059,7 +2067,7 @@ int launch(const skv::Geometry& g, int kind, Kernel kernel, dim3 grid, size_t ld
   auto* st = (DevState*)g.dev;
   hipStream_t stream = (hipStream_t)g.stream;
   hipEvent_t a = nullptr, b = nullptr;
-  if (st && (st->timing >> kind & 1)) {
+  if (st && kind >= 0 && (st->timing >> kind & 1)) {
     a = st->get();
     b = st->get();
   }
@@ -2083,11 +2091,11 @@ int group_limit(const skv::Geometry& g) { return skv::decode_group_limit(g.N, g.
 int w_of(const skv::Geometry& g) { return g.D + g.r + 4; }
 
 template <int D, int RB, int MB>
-int launch_split_t(const skv::Geometry& g, const DecodeParams& p, int items) {
+int launch_split_t(const skv::Geometry& g, const DecodeParams& p, int items, bool timed) {
   constexpr int DB = D / 16, NQ = DB + MB;
   size_t lds = (size_t)2 * RB * (NQ * 64 * 16 + 2 * 64 * 4);          // two slots of wave states
   if (p.n_app > 0) lds = std::max(lds, (size_t)64 * (128 + 8) * 2);  // append blocks' staging
-  return launch(g, 2, decode_split_kernel<D, RB, MB>, dim3(p.n_app + items), lds, p,
+  return launch(g, timed ? 2 : -1, decode_split_kernel<D, RB, MB>, dim3(p.n_app + items), lds, p,
                 "decode_split_kernel");
 }
 
@@ -2129,16 +2137,16 @@ int prefill_split(int nblk, int min_view_pages) {
 }
 
 template <int D>
-int launch_split_d(const skv::Geometry& g, int rb, int mb, const DecodeParams& p, int items) {
-  if (rb == 1 && mb == 1) return launch_split_t<D, 1, 1>(g, p, items);
-  if (rb == 1 && mb == 2) return launch_split_t<D, 1, 2>(g, p, items);
-  if (rb == 1 && mb == 4) return launch_split_t<D, 1, 4>(g, p, items);
-  if (rb == 1 && mb == 8) return launch_split_t<D, 1, 8>(g, p, items);
-  if (rb == 2 && mb == 1) return launch_split_t<D, 2, 1>(g, p, items);
-  if (rb == 2 && mb == 2) return launch_split_t<D, 2, 2>(g, p, items);
-  if (rb == 2 && mb == 4) return launch_split_t<D, 2, 4>(g, p, items);
-  if (rb == 4 && mb == 1) return launch_split_t<D, 4, 1>(g, p, items);
-  if (rb == 4 && mb == 2) return launch_split_t<D, 4, 2>(g, p, items);
+int launch_split_d(const skv::Geometry& g, int rb, int mb, const DecodeParams& p, int items, bool timed) {
+  if (rb == 1 && mb == 1) return launch_split_t<D, 1, 1>(g, p, items, timed);
+  if (rb == 1 && mb == 2) return launch_split_t<D, 1, 2>(g, p, items, timed);
+  if (rb == 1 && mb == 4) return launch_split_t<D, 1, 4>(g, p, items, timed);
+  if (rb == 1 && mb == 8) return launch_split_t<D, 1, 8>(g, p, items, timed);
+  if (rb == 2 && mb == 1) return launch_split_t<D, 2, 1>(g, p, items, timed);
+  if (rb == 2 && mb == 2) return launch_split_t<D, 2, 2>(g, p, items, timed);
+  if (rb == 2 && mb == 4) return launch_split_t<D, 2, 4>(g, p, items, timed);
+  if (rb == 4 && mb == 1) return launch_split_t<D, 4, 1>(g, p, items, timed);
+  if (rb == 4 && mb == 2) return launch_split_t<D, 4, 2>(g, p, items, timed);
   snprintf(g_err, sizeof g_err, "no decode kernel for rb=%d mb=%d", rb, mb);
   return SKV_ERR_UNSUPPORTED;
 }
@@ -2167,7 +2175,31 @@ int dev_init(Geometry& g) {
     set_err("hipMemsetAsync", e);
     return SKV_ERR_HIP;
   }
-  g.dev = new DevState();
+  // the static scratch's device address on the current device, once per device
+  static std::mutex mu;
+  static float* addr[64] = {};
+  int dev = 0;
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= 64) {
+    set_err("hipGetDevice", e);
+    return SKV_ERR_HIP;
+  }
+  float* ptr = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+      e = hipGetSymbolAddress((void**)&addr[dev], HIP_SYMBOL(scratch));
+      if (e != hipSuccess) {
+        addr[dev] = nullptr;
+        set_err("hipGetSymbolAddress(scratch)", e);
+        return SKV_ERR_HIP;
+      }
+    }
+    ptr = addr[dev];
+  }
+  auto* st = new DevState();
+  st->scratch_static = ptr;
+  g.dev = st;
   return SKV_OK;
 }
 
@@ -2260,11 +2292,9 @@ int dev_project(const Geometry& g, const ProjectJob& job) {
 // Decode for the agents of job, in groups that fit one launch. With app (a
 // fused decode step) each group's split launch also writes the group's new
 // rows and the merge adds the new tokens.
-static int decode_impl(const Geometry& g, const AttnJob& job, const AppendJob* app) {
+static int decode_impl(const Geometry& g, const AttnJob& job, const AppendJob* app, float* part, bool timed) {
   const int ng = group_limit(g);
-  hipStream_t st = (hipStream_t)g.stream;
   const int W = w_of(g);
-  float* part = (float*)(g.arena + g.scratch_off);
   for (int a0 = 0; a0 < job.n; a0 += ng) {
     const int n = std::min(ng, job.n - a0);
     DecodeParams p{};
@@ -2364,7 +2394,7 @@ static int decode_impl(const Geometry& g, const AttnJob& job, const AppendJob* a
     const int items = items_per_head * g.Hkv;
     int rc = SKV_OK;
     if (p.n_app + items > 0)
-      rc = g.D == 128 ? launch_split_d<128>(g, rb, mb, p, items) : launch_split_d<64>(g, rb, mb, p, items);
+      rc = g.D == 128 ? launch_split_d<128>(g, rb, mb, p, items, timed) : launch_split_d<64>(g, rb, mb, p, items, timed);
     if (rc != SKV_OK) return rc;
     MergeParams mp{};
     mp.part = part;
@@ -2401,8 +2431,9 @@ static int decode_impl(const Geometry& g, const AttnJob& job, const AppendJob* a
     }
     mp.n_rows = n * g.Hkv * g.G;
     const size_t mlds = mp.n_app ? (size_t)64 * (128 + 8) * 2 : 0;
-    rc = g.D == 128 ? launch(g, 3, decode_merge_kernel<128>, dim3(mp.n_rows + mp.n_app), mlds, mp, "decode_merge_kernel")
-                    : launch(g, 3, decode_merge_kernel<64>, dim3(mp.n_rows + mp.n_app), mlds, mp, "decode_merge_kernel");
+    const int kind = timed ? 3 : -1;
+    rc = g.D == 128 ? launch(g, kind, decode_merge_kernel<128>, dim3(mp.n_rows + mp.n_app), mlds, mp, "decode_merge_kernel")
+                    : launch(g, kind, decode_merge_kernel<64>, dim3(mp.n_rows + mp.n_app), mlds, mp, "decode_merge_kernel");
     if (rc != SKV_OK) return rc;
   }
   return SKV_OK;
@@ -2458,10 +2489,21 @@ int dev_probe_mfma_bf16(void* stream, double* tflops) {
   return SKV_OK;
 }
 
-int dev_attn_decode(const Geometry& g, const AttnJob& job) { return decode_impl(g, job, nullptr); }
+float* arena_partials(const Geometry& g) { return (float*)(g.arena + g.scratch_off); }
+
+int dev_attn_decode(const Geometry& g, const AttnJob& job) {
+  return decode_impl(g, job, nullptr, arena_partials(g), true);
+}
 
 int dev_decode_step(const Geometry& g, const AttnJob& job, const AppendJob& app) {
-  return decode_impl(g, job, &app);
+  return decode_impl(g, job, &app, arena_partials(g), true);
+}
+
+// The partial rows go to the static scratch (the runtime has checked that the
+// call's largest launch fits it); nothing is allocated and no events recorded.
+int dev_decode_step_static(const Geometry& g, const AttnJob& job, const AppendJob& app) {
+  auto* st = (DevState*)g.dev;
+  return decode_impl(g, job, &app, st->scratch_static, false);
 }
 
 int dev_attn_prefill(const Geometry& g, const AttnJob& job) {

@@ -81,6 +81,23 @@ inline int plan_check_decode(const Geometry& g, const AttnJob& job, bool step, c
   return SKV_OK;
 }
 
+// Bytes of decode partial rows the largest launch of a decode call writes:
+// items x (agents x G) rows x (d + r + 4) fp32 values.
+inline uint64_t decode_partial_bytes(const Geometry& g, const AttnJob& job, bool step) {
+  const int ng = decode_group_limit(g.N, g.G, g.mode, g.r);
+  uint64_t most = 0;
+  for (int a0 = 0; ng > 0 && a0 < job.n; a0 += ng) {
+    const int n = std::min(ng, job.n - a0);
+    const int I = decode_items_per_head(decode_group_chunks(job.ag + a0, n), step ? n : 0, g.Hkv);
+    if (I > 0) most = std::max(most, (uint64_t)I * g.Hkv * n * g.G * (g.D + g.r + 4) * sizeof(float));
+  }
+  return most;
+}
+
+// Size of the library's static device scratch (the partial rows of the
+// decode entry point that allocates nothing, skv_decode_step_static).
+constexpr uint64_t kStaticScratchBytes = 16ull << 20;
+
 // SKV_OK if every agent's view of a prefill call fits the prefill kernel's
 // page list (4096 pages of 64 rows: 262,144 rows, shared and own pages
 // counted separately).

@@ -500,10 +500,12 @@ int skv_attn_decode(skv_ctx* c, int layer, int n, const int* agents, const int* 
   return SKV_OK;
 }
 
-int skv_decode_step(skv_ctx* c, int layer, int n, const int* agents, const int* base_len,
-                    const int* suffix_len, const skv_bf16* k, const skv_bf16* v,
-                    const skv_bf16* x, const skv_bf16* A, const skv_bf16* q, const skv_bf16* B,
-                    skv_bf16* o) {
+// Fused decode step; with scratch_static the launches keep their partial
+// rows in the library's static device scratch instead of the arena.
+static int decode_step(skv_ctx* c, int layer, int n, const int* agents, const int* base_len,
+                       const int* suffix_len, const skv_bf16* k, const skv_bf16* v, const skv_bf16* x,
+                       const skv_bf16* A, const skv_bf16* q, const skv_bf16* B, skv_bf16* o,
+                       bool scratch_static) {
   if (!c) return SKV_ERR_ARG;
   const Geometry& g = c->g;
   if (layer < 0 || layer >= g.L) return c->fail(SKV_ERR_ARG, "layer %d out of range", layer);
@@ -544,6 +546,10 @@ int skv_decode_step(skv_ctx* c, int layer, int n, const int* agents, const int* 
   char msg[256];
   int rc = skv::plan_check_decode(g, job, true, msg, sizeof msg);
   if (rc != SKV_OK) return c->fail(rc, "%s", msg);
+  if (scratch_static && skv::decode_partial_bytes(g, job, true) > skv::kStaticScratchBytes)
+    return c->fail(SKV_ERR_UNSUPPORTED, "decode partial rows (%llu bytes) exceed the static scratch (%llu bytes)",
+                   (unsigned long long)skv::decode_partial_bytes(g, job, true),
+                   (unsigned long long)skv::kStaticScratchBytes);
   std::vector<std::vector<int32_t>> tables(n);
   std::vector<int32_t> taken;
   for (int i = 0; i < n; ++i) {
@@ -584,7 +590,7 @@ int skv_decode_step(skv_ctx* c, int layer, int n, const int* agents, const int* 
   job.q = q;
   job.B = B;
   job.o = o;
-  rc = skv::dev_decode_step(g, job, app);
+  rc = scratch_static ? skv::dev_decode_step_static(g, job, app) : skv::dev_decode_step(g, job, app);
   if (rc != SKV_OK) {
     for (int32_t p : taken) l.free.insert(p);
     return c->fail(rc, "device decode step failed: %s", skv::dev_last_error());
@@ -599,6 +605,18 @@ int skv_decode_step(skv_ctx* c, int layer, int n, const int* agents, const int* 
   c->counters.base_rows_own += n;
   (x ? c->counters.lr_rows : c->counters.lr_zero_rows) += n;
   return SKV_OK;
+}
+
+int skv_decode_step(skv_ctx* c, int layer, int n, const int* agents, const int* base_len,
+                    const int* suffix_len, const skv_bf16* k, const skv_bf16* v, const skv_bf16* x,
+                    const skv_bf16* A, const skv_bf16* q, const skv_bf16* B, skv_bf16* o) {
+  return decode_step(c, layer, n, agents, base_len, suffix_len, k, v, x, A, q, B, o, false);
+}
+
+int skv_decode_step_static(skv_ctx* c, int layer, int n, const int* agents, const int* base_len,
+                           const int* suffix_len, const skv_bf16* k, const skv_bf16* v, const skv_bf16* x,
+                           const skv_bf16* A, const skv_bf16* q, const skv_bf16* B, skv_bf16* o) {
+  return decode_step(c, layer, n, agents, base_len, suffix_len, k, v, x, A, q, B, o, true);
 }
 
 int skv_pack_qkv(skv_ctx* c, const skv_bf16* w_qkv, skv_bf16* w_packed) {

@@ -60,6 +60,7 @@ EXPORTS = {
     "skv_attn_prefill": (_I, [_P, _I, _I, _IP, _IP, _IP, _IP, _P, _P, _P]),
     "skv_attn_decode": (_I, [_P, _I, _I, _IP, _IP, _IP, _P, _P, _P]),
     "skv_decode_step": (_I, [_P, _I, _I, _IP, _IP, _IP, _P, _P, _P, _P, _P, _P, _P]),
+    "skv_decode_step_static": (_I, [_P, _I, _I, _IP, _IP, _IP, _P, _P, _P, _P, _P, _P, _P]),
     "skv_crop": (_I, [_P, _I, _I]),
     "skv_set_lr_begin": (_I, [_P, _I, _I]),
     "skv_project_append": (_I, [_P, _I, _I, _IP, _IP, _P, _P, _P, ctypes.c_float, _P]),
@@ -276,6 +277,19 @@ def skv_decode_step(ctx: Ctx, layer: int, agents, base_len, suffix_len, k, v, x,
     kv = (n, ctx.Hkv, ctx.d)
     qs = (n, ctx.Hq, ctx.d)
     ctx._check(ctx.lib.skv_decode_step(
+        ctx.handle, layer, n, ag, bl, sl, _ptr(k, kv, "k"), _ptr(v, kv, "v"),
+        _ptr(x, (n, ctx.hidden), "x"), _ptr(A, ctx.a_shape, "A"), _ptr(q, qs, "q"),
+        _ptr(B, ctx.b_shape, "B"), _ptr(o, qs, "o")))
+
+
+def skv_decode_step_static(ctx: Ctx, layer: int, agents, base_len, suffix_len, k, v, x, A, q, B, o):
+    """skv_decode_step with the partial rows in the library's static device scratch."""
+    ag, n = _ints(agents)
+    bl, _ = _ints(base_len)
+    sl, _ = _ints(suffix_len)
+    kv = (n, ctx.Hkv, ctx.d)
+    qs = (n, ctx.Hq, ctx.d)
+    ctx._check(ctx.lib.skv_decode_step_static(
         ctx.handle, layer, n, ag, bl, sl, _ptr(k, kv, "k"), _ptr(v, kv, "v"),
         _ptr(x, (n, ctx.hidden), "x"), _ptr(A, ctx.a_shape, "A"), _ptr(q, qs, "q"),
         _ptr(B, ctx.b_shape, "B"), _ptr(o, qs, "o")))

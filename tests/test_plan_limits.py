@@ -124,3 +124,33 @@ def test_misaligned_device_pointers_are_rejected(ctx):
         assert e.value.code == "ARG", (fn.__name__, e.value)
         assert state(ctx) == before
     B.skv_crop(ctx, 0, 0)
+
+
+def test_static_scratch_limit():
+    """skv_decode_step_static keeps the decode partial rows in a 16 MiB static
+    array: a launch needing more is refused before anything is enqueued, while
+    the arena-backed skv_decode_step takes the same call."""
+    cfg = dict(n_layers=1, n_q_heads=64, n_kv_heads=64, head_dim=128, hidden=64, rank=32, n_agents=16,
+               mode=1, page_size=64, max_pages=7200)
+    n = B.skv_arena_bytes(cfg, "host")
+    c = B.skv_create(cfg, (1 << 24, n), None, "host")
+    P = 450_000  # 14,063 chunks per KV head: 28 items of <= 512 chunks, 64 heads
+    B.skv_append_base(c, 0, -1, FAKE, FAKE, n=P)
+    B.skv_append_lowrank(c, 0, -1, 0, P, None, None)
+    agents = list(range(16))
+    for a in agents:
+        B.skv_crop(c, a, P)
+    # 28 items x 64 heads x 16 rows x (128 + 32 + 4) x 4 bytes = 18.8 MB > 16 MiB
+    before = state16(c)
+    with pytest.raises(B.SkvError) as e:
+        B.skv_decode_step_static(c, 0, agents, [P] * 16, [0] * 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert e.value.code == "UNSUPPORTED" and "static scratch" in str(e.value)
+    assert state16(c) == before
+    # one agent: 28 x 64 x 1 x 164 x 4 bytes = 1.2 MB fits
+    B.skv_decode_step_static(c, 0, [0], [P], [0], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    # the arena path takes the 16-agent call
+    B.skv_decode_step(c, 0, agents, [P] * 16, [1] + [0] * 15, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+
+
+def state16(c):
+    return (B.skv_get_lens(c, 0), B.skv_get_counters(c), [B.skv_get_pages(c, 0, s) for s in range(-1, 16)])
