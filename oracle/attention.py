@@ -59,18 +59,24 @@ def attend_view(q: np.ndarray, k: np.ndarray, v: np.ndarray, positions) -> np.nd
     q [n][Hq][d], k [L][Hkv][d], v [L][Hkv][dv] (already materialised for this agent),
     positions: length-n view positions t (each query sees rows 0..t).
     Returns o [n][Hq][d] in float64.
+
+    The definition in matrix form, one query head at a time: S = Q K^T / sqrt(d)
+    over the view, keys after a query's position set to -inf, a softmax over
+    each row, O = P V.
     """
     n, hq, d = q.shape
     hkv = k.shape[1]
     group = hq // hkv
     scale = 1.0 / np.sqrt(d)
+    pos = np.asarray(positions, dtype=np.int64)
+    Lv = int(pos.max()) + 1
+    after = np.arange(Lv)[None, :] > pos[:, None]   # key j lies after query i's position
     o = np.empty((n, hq, v.shape[2]))
-    for i, t in enumerate(positions):
-        for h in range(hq):
-            g = kv_head_of(h, group)
-            s = (k[: t + 1, g, :] @ q[i, h, :]) * scale
-            p = softmax_rows(s[None, :])[0]
-            o[i, h, :] = p @ v[: t + 1, g, :]
+    for h in range(hq):
+        g = kv_head_of(h, group)
+        s = (q[:, h, :] @ k[:Lv, g, :].T) * scale
+        s[after] = -np.inf
+        o[:, h, :] = softmax_rows(s) @ v[:Lv, g, :]
     return o
 
 

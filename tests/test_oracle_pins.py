@@ -315,19 +315,24 @@ def _mut_lr_sign(v_base, lr_rows, b_agent):
 
 
 def _make_attend_mut(kind):
+    # the oracle's matrix form with one plausible mistake: the causal mask one
+    # key short (a query does not see its own position), or a 1/d scale
     def attend(q, k, v, positions):
         n, hq, d = q.shape
         hkv = k.shape[1]
         group = hq // hkv
         scale = 1.0 / d if kind == "scale" else 1.0 / np.sqrt(d)
+        pos = np.asarray(positions, dtype=np.int64)
+        Lv = int(pos.max()) + 1
+        after = np.arange(Lv)[None, :] > pos[:, None]
+        if kind == "causal":
+            after = np.arange(Lv)[None, :] >= np.maximum(pos[:, None], 1)
         o = np.empty((n, hq, v.shape[2]))
-        for i, t in enumerate(positions):
-            end = t if kind == "causal" and t > 0 else t + 1
-            for h in range(hq):
-                g = oatt.kv_head_of(h, group)
-                s = (k[:end, g, :] @ q[i, h, :]) * scale
-                p = oatt.softmax_rows(s[None, :])[0]
-                o[i, h, :] = p @ v[:end, g, :]
+        for h in range(hq):
+            g = oatt.kv_head_of(h, group)
+            s = (q[:, h, :] @ k[:Lv, g, :].T) * scale
+            s[after] = -np.inf
+            o[:, h, :] = oatt.softmax_rows(s) @ v[:Lv, g, :]
         return o
     return attend
 
