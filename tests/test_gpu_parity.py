@@ -125,7 +125,7 @@ def test_tiny_full_schedule():
     assert len(res) == 2 + 16
 
 
-@pytest.mark.parametrize("prefix", [1024, 2048])
+@pytest.mark.parametrize("prefix", [1024, 2048, 4096])
 def test_qwen25_turns_with_handoff(prefix):
     R = _runner()
     sc = synth.qwen25_schedule(prefix=prefix, decode_sample=[0, 1, 63, 127])
@@ -135,16 +135,14 @@ def test_qwen25_turns_with_handoff(prefix):
 def test_qwen25_8k_prefix():
     R = _runner()
     sc = synth.qwen25_schedule(prefix=8192, turns=2, decode=8, decode_sample=[0, 7])
-    R.run_parity(sc, sample_rows=lambda ev: list(range(0, sum(ev.n_q), 37)) + [sum(ev.n_q) - 1],
-                 log=log)
+    R.run_parity(sc, log=log)
 
 
 @pytest.mark.parametrize("takeover", [0, 160, 320])
 def test_qwen3_takeover(takeover):
     R = _runner()
     sc = synth.qwen3_schedule(takeover=takeover, decode=6)
-    R.run_parity(sc, sample_rows=lambda ev: list(range(0, sum(ev.n_q), 23)) + [sum(ev.n_q) - 1],
-                 log=log)
+    R.run_parity(sc, log=log)
 
 
 def test_llama3_suffix_prefill_at_32k():
@@ -158,6 +156,16 @@ def test_llama3_suffix_prefill_at_32k():
     assert sum(1 for r in res if r[1] == "prefill") == 1
 
 
+def test_llama3_suffix_prefill_at_32k_every_row():
+    """The timed suffix prefill (4 agents x 512 own tokens over the 32,768-token
+    shared prefix, llama3 shapes, in its own launch shape), every one of its
+    2,048 query rows against the oracle."""
+    R = _runner()
+    sc = synth.llama3_schedule(prefix=32768, prefill=512, decode=0, seed=1013)
+    _, _, res = R.run_parity(sc, log=log)
+    assert [r[1] for r in res] == ["prefill"]
+
+
 @pytest.mark.parametrize("prefix,steps", [(33792, 3), (67584, 2)])
 def test_llama3_long_prefix_decode(prefix, steps):
     R = _runner()
@@ -166,10 +174,14 @@ def test_llama3_long_prefix_decode(prefix, steps):
 
 
 def test_many_agent_mixed_turns():
+    """All six turns of the many-agent workload (one layer): four agents
+    prefill 512 own tokens while four decode, then the lead agent crops 256
+    own rows and re-appends them as canonical rows, so later turns crop agents
+    that were cropped and re-appended before. Every query row is compared."""
     R = _runner()
-    sc = synth.many_schedule(turns=2)
-    samp = lambda ev: (list(range(0, sum(ev.n_q), 97)) + [sum(ev.n_q) - 1]) if ev.kind == "prefill" else None
-    R.run_parity(sc, sample_rows=samp, log=log)
+    sc = synth.many_schedule(turns=6)
+    _, _, res = R.run_parity(sc, log=log)
+    assert len(res) == 12
 
 
 # --------------------------------------------------------------------------
@@ -318,6 +330,83 @@ def test_h1_session_with_offsets_and_accounting():
     for k, v in orc.counters.items():
         assert got[k] == v, (k, got[k], v)
     assert orc.counters["rows_cropped"] == 2 * N * 20 and orc.counters["lr_zero_rows"] >= 2 * N * 20
+
+
+@pytest.mark.parametrize("shape_name", ["llama3", "qwen3"])
+def test_canonical_recompute_equals_fresh_appends(shape_name):
+    """RoleKV ("How we built it": a hand-off crops the cache and recomputes the
+    tokens canonically, which must equal a fresh base prefill of them).
+    Context A: agent 0 appends 300 own rows with its adapter (x A), crops back
+    to 100 (mid-page: three pages freed, the kept page holds stale slots), agent
+    1 takes a freed page, then agent 0 re-appends the 200 tokens as canonical
+    rows (the same base K/V, zero low-rank rows). Context B appends the same
+    rows fresh, with no crop (so its page ids differ). Every live K/V byte and low-rank row is equal,
+    decode and prefill outputs are equal bit for bit, and context A matches
+    the oracle."""
+    import torch
+    from lora_shared_kv_amd import skv as B
+    R = _runner()
+    shape = synth.WORKLOADS[shape_name]
+    N, Hkv, d = shape.n_agents, shape.n_kv_heads, shape.head_dim
+    dr = synth.Draws(4242)
+    P = 1000
+    kp, vp, xp = dr.normal((P, Hkv, d)), dr.normal((P, Hkv, d)), dr.normal((P, shape.hidden))
+    if shape.mode == synth.BASE_SHARED:
+        A = dr.normal((N, shape.hidden, shape.rank), 1.0 / shape.hidden)
+    else:
+        A = dr.normal((shape.hidden, shape.rank), 1.0 / shape.hidden)
+    Bw = dr.normal((N, shape.rank, Hkv * d), 0.01 / shape.rank)
+    ko, vo, xo = dr.normal((300, Hkv, d)), dr.normal((300, Hkv, d)), dr.normal((300, shape.hidden))
+    k1, v1, x1 = dr.normal((80, Hkv, d)), dr.normal((80, Hkv, d)), dr.normal((80, shape.hidden))
+    a_of = (lambda p: A[p]) if shape.mode == synth.BASE_SHARED else (lambda p: A)
+    head = [synth.AppendBase(0, -1, kp, vp)] + [
+        synth.AppendLowrank(0, -1, p, P, xp, a_of(p)) for p in range(synth.n_planes(shape))] + [
+        synth.Crop(a, P) for a in range(N)] + [
+        synth.AppendAgents(0, [1], [60], k1[:60], v1[:60], x1[:60], A)]
+    evA = head + [synth.AppendAgents(0, [0], [300], ko, vo, xo, A), synth.Crop(0, P + 100),
+                  synth.AppendAgents(0, [1], [20], k1[60:], v1[60:], x1[60:], A),
+                  synth.AppendAgents(0, [0], [200], ko[100:], vo[100:], None, None)]
+    evB = head + [synth.AppendAgents(0, [0], [100], ko[:100], vo[:100], xo[:100], A),
+                  synth.AppendAgents(0, [0], [200], ko[100:], vo[100:], None, None),
+                  synth.AppendAgents(0, [1], [20], k1[60:], v1[60:], x1[60:], A)]
+    q_dec = dr.normal((2, shape.n_q_heads, d))
+    q_pre = dr.normal((64, shape.n_q_heads, d))
+    tail = [synth.Attend("decode", 0, [0, 1], [P, P], [300, 80], [1, 1], q_dec, Bw, "decode after hand-off"),
+            synth.Attend("prefill", 0, [0], [P], [300], [64], q_pre, Bw, "prefill after hand-off")]
+    sc = synth.Schedule(shape, 1, n_layers=1)
+    sc.events = evA + tail
+    gA, orc, resA = R.run_parity(sc, max_pages=64, log=log)
+    gB = R.GpuRun(sc, max_pages=64)
+    for ev in evB:
+        gB.apply(ev)
+    outB = [gB.apply(ev) for ev in tail]
+    B.skv_sync(gB.ctx)
+    # the same live bytes, read through each context's page tables
+    ki, vi = k_tile_index(d), v_tile_index(d)
+    pools = {}
+    for name, g in (("A", gA), ("B", gB)):
+        K, VT, LRT = (t.cpu().numpy().view(np.uint16) for t in _pool_views(g))
+        rows = {}
+        for seq, n in ((-1, P), (0, 300), (1, 80)):
+            pages = B.skv_get_pages(g.ctx, 0, seq)
+            kk = np.stack([K[0, pages[j // 64]][:, ki[j % 64]] for j in range(n)])
+            vv = np.stack([VT[0, pages[j // 64]][:, vi[j % 64]] for j in range(n)])
+            pl = 0 if seq == -1 or shape.mode == synth.BASE_LR_SHARED else seq
+            lr = np.stack([LRT[pl, 0, pages[j // 64], :, j % 64] for j in range(n)])
+            rows[seq] = (kk, vv, lr)
+        pools[name] = rows
+    for seq in (-1, 0, 1):
+        for a, b in zip(pools["A"][seq], pools["B"][seq]):
+            assert np.array_equal(a, b), seq
+    assert np.all(pools["A"][0][2][100:] == 0)          # the recomputed tokens carry no low-rank term
+    assert B.skv_get_lens(gA.ctx, 0) == B.skv_get_lens(gB.ctx, 0)
+    # agent 1 took a page agent 0 freed, so the page ids differ between the contexts
+    assert B.skv_get_pages(gA.ctx, 0, 1) != B.skv_get_pages(gB.ctx, 0, 1)
+    assert [r[0] for r in resA] == ["decode after hand-off", "prefill after hand-off"]
+    # bit-identical attention over the two caches
+    oa = [gA.apply(ev) for ev in tail]
+    for x, y in zip(oa, outB):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
 def test_lr_only_term():
