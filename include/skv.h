@@ -90,17 +90,25 @@ typedef struct skv_config {
 
 typedef struct skv_ctx skv_ctx;
 
-/* Bytes of device memory skv_create needs for cfg (0 if cfg is invalid). */
+/* Bytes of device memory skv_create needs for cfg (0 if cfg is invalid): the
+ * K/V and low-rank pools, page tables and scratch. Sized up front so the store
+ * is one physically shared allocation (paperlayer summary of arXiv
+ * 2609.17109, Sec. 3.2 and Table 2: without a shared paged store the prefix
+ * was copied per branch and peak memory fell only 5-12%). */
 size_t skv_arena_bytes(const skv_config* cfg);
 
 /* Create a context over a caller-owned device arena of at least
- * skv_arena_bytes(cfg) bytes (256-byte aligned). stream is a hipStream_t
+ * skv_arena_bytes(cfg) bytes (256-byte aligned). The configuration carries the
+ * quantities the pages state the problem in: the rank r, shared-A versus
+ * per-agent-A (LRAgent review, "The reading" and Figs. 2-3: BaseShared and
+ * BaseLRShared), the agents, and the GQA head groups. stream is a hipStream_t
  * (NULL = default stream). Errors: ARG (bad config, small arena),
  * UNSUPPORTED (page_size or shape the device code does not handle). */
 int skv_create(const skv_config* cfg, void* dev_arena, size_t arena_bytes, void* stream,
                skv_ctx** out);
 
-/* Free host metadata. Does not touch the arena. NULL is allowed. */
+/* Free host metadata (the counterpart of skv_create). Does not touch the
+ * arena, which stays the caller's. NULL is allowed. */
 void skv_destroy(skv_ctx* ctx);
 
 /* a1 / a3: append n rows of base-weight K and V to the end of sequence seq at
@@ -250,16 +258,24 @@ int skv_set_lr_begin(skv_ctx* ctx, int agent, int pos);
  * bytes. Errors: ARG, STATE. */
 int skv_crop(skv_ctx* ctx, int seq, int new_len);
 
-/* Lengths at one layer. Any output pointer may be NULL. base_len, suffix_len,
- * lr_own: host [N]; lr_shared: host [planes]. P receives the shared length. */
+/* Lengths at one layer, for checking the cache's state from outside (RoleKV
+ * write-up, "How we built it": cache-equivalence and canonicalization tests;
+ * "Challenges we ran into": the offsets a caller passes must match the
+ * cache). Any output pointer may be NULL. base_len, suffix_len, lr_own: host
+ * [N]; lr_shared: host [planes]. P receives the shared length. */
 int skv_get_lens(const skv_ctx* ctx, int layer, int* P, int* base_len, int* suffix_len,
                  int* lr_shared, int* lr_own);
 
-/* Page ids of seq at layer, in order, into host ids[cap]. Returns the count
- * (which may exceed cap) or a negative error. */
+/* Page ids of seq at layer, in order, into host ids[cap]: with skv_get_pools,
+ * the means to check that agents resolve the shared prefix to the same
+ * physical pages (paperlayer summary of arXiv 2609.17109, App. C: physical
+ * sharing is checked by the identity of the prefix tensors' storage). Returns
+ * the count (which may exceed cap) or a negative error. */
 int skv_get_pages(const skv_ctx* ctx, int layer, int seq, int32_t* ids, int cap);
 
-/* Device pool layout, for byte-level inspection:
+/* Device pool layout, for byte-level inspection (the storage-identity check
+ * of paperlayer App. C; the canonicalization test of RoleKV "How we built
+ * it" compares a recomputed cache with a fresh one byte by byte):
  *   K  [layer][page][Hkv][64 * d]              bf16 tiles, see below
  *   V  [layer][page][Hkv][64 * d]              bf16 tiles, see below
  *   LRT[plane][layer][page][r][page_size]      bf16 (low-rank rows transposed)
@@ -277,7 +293,10 @@ typedef struct skv_pools {
 } skv_pools;
 int skv_get_pools(const skv_ctx* ctx, skv_pools* out);
 
-/* Token accounting (RoleKV "Challenges": honest cost accounting). */
+/* Token accounting: rows appended to the shared and own sequences, low-rank
+ * and zero low-rank rows, rows cropped, pages, launches (RoleKV write-up,
+ * "Challenges we ran into": count the canonicalization tokens; "How we built
+ * it": prefill, reuse and canonicalization tokens are logged per turn). */
 typedef struct skv_counters {
   int64_t base_rows_shared, base_rows_own, lr_rows, lr_zero_rows, rows_cropped;
   int64_t pages_alloc, pages_freed, launches;
@@ -299,10 +318,15 @@ int skv_set_timing(skv_ctx* ctx, int enable);
 /* Waits for the stream, sums the recorded intervals, and clears them. */
 int skv_collect_timing(skv_ctx* ctx, skv_kernel_times* out);
 
-/* Wait for all work enqueued by this context. Errors: HIP. */
+/* Wait for all work enqueued by this context; device faults surface here
+ * (every other call validates on the host and only enqueues: RoleKV
+ * "Challenges we ran into": no state that silently diverges from what the
+ * caller passed). Errors: HIP. */
 int skv_sync(skv_ctx* ctx);
 
-/* Message of the last failed call on ctx ("" if none). */
+/* Message of the last failed call on ctx ("" if none): which argument or
+ * length disagreed with the cache (RoleKV "Challenges we ran into": a wrong
+ * offset must fail loudly, not turn the adapter off). */
 const char* skv_last_error(const skv_ctx* ctx);
 
 /* Measurement probes (no context; the current device; synchronous on

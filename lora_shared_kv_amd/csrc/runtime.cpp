@@ -181,10 +181,13 @@ int run_jobs(skv_ctx* c, const std::vector<AppendJob>& jobs) {
   return SKV_OK;
 }
 
-// Checks shared by the calls that append own rows to listed agents: layer,
-// distinct agents, counts, and low-rank rows level with base rows. total gets
-// the row count.
-int check_agent_rows(skv_ctx* c, int layer, int n, const int* agents, const int* counts, long* total) {
+// Checks shared by the calls that append own rows to listed agents, in the
+// order every call follows (arguments, then state, then pages): layer,
+// distinct agents, counts; for a call with rows, arg_err (the caller's
+// pointer and argument checks, nullptr if they passed); then low-rank rows
+// level with base rows. total gets the row count.
+int check_agent_rows(skv_ctx* c, int layer, int n, const int* agents, const int* counts, long* total,
+                     const char* arg_err) {
   const Geometry& g = c->g;
   *total = 0;
   if (layer < 0 || layer >= g.L) return c->fail(SKV_ERR_ARG, "layer %d out of range", layer);
@@ -205,6 +208,7 @@ int check_agent_rows(skv_ctx* c, int layer, int n, const int* agents, const int*
     tot += counts[i];
   }
   if (tot == 0) return SKV_OK;
+  if (arg_err) return c->fail(SKV_ERR_ARG, "%s", arg_err);
   const Layer& l = c->layers[layer];
   for (int i = 0; i < n; ++i) {
     int slot = 1 + agents[i];
@@ -417,12 +421,12 @@ int skv_append_agents(skv_ctx* c, int layer, int n, const int* agents, const int
                       const skv_bf16* A) {
   if (!c) return SKV_ERR_ARG;
   if (x && !A) return c->fail(SKV_ERR_ARG, "x given without A");
+  const char* arg_err = (!k || !v) ? "null k or v"
+                        : !aligned16({k, v, x, x ? A : nullptr}) ? "k, v, x and A must be 16-byte aligned"
+                                                                 : nullptr;
   long total = 0;
-  int rc = check_agent_rows(c, layer, n, agents, counts, &total);
+  int rc = check_agent_rows(c, layer, n, agents, counts, &total, arg_err);
   if (rc != SKV_OK || total == 0) return rc;
-  if (!k || !v) return c->fail(SKV_ERR_ARG, "null k or v");
-  if (!aligned16({k, v, x, x ? A : nullptr}))
-    return c->fail(SKV_ERR_ARG, "k, v, x and A must be 16-byte aligned");
   AgentRows ar;
   rc = plan_agent_rows(c, layer, n, agents, counts, k, v, x, A, ar);
   if (rc != SKV_OK) return rc;
@@ -636,13 +640,14 @@ int skv_project_append(skv_ctx* c, int layer, int n, const int* agents, const in
                        const skv_bf16* x, const skv_bf16* w_packed, const skv_bf16* A, float rope_theta,
                        skv_bf16* q_out) {
   if (!c) return SKV_ERR_ARG;
+  const char* arg_err = (!x || !w_packed || !q_out) ? "null x, w_packed or q_out"
+                        : !aligned16({x, w_packed, A, q_out}) ? "device pointers must be 16-byte aligned"
+                        : !(rope_theta == 0.f || (rope_theta > 1.f && rope_theta < 1e30f))
+                            ? "rotary base must be 0 or above 1 (and finite)"
+                            : nullptr;
   long total = 0;
-  int rc = check_agent_rows(c, layer, n, agents, counts, &total);
+  int rc = check_agent_rows(c, layer, n, agents, counts, &total, arg_err);
   if (rc != SKV_OK || total == 0) return rc;
-  if (!x || !w_packed || !q_out) return c->fail(SKV_ERR_ARG, "null x, w_packed or q_out");
-  if (!aligned16({x, w_packed, A, q_out})) return c->fail(SKV_ERR_ARG, "device pointers must be 16-byte aligned");
-  if (!(rope_theta == 0.f || (rope_theta > 1.f && rope_theta < 1e30f)))
-    return c->fail(SKV_ERR_ARG, "rotary base %g (0 or above 1)", (double)rope_theta);
   AgentRows ar;
   rc = plan_agent_rows(c, layer, n, agents, counts, nullptr, nullptr, A ? x : nullptr, A, ar);
   if (rc != SKV_OK) return rc;

@@ -107,6 +107,40 @@ class GpuRun:
         return None
 
 
+def lowrank_chain(hidden: int) -> int:
+    """Longest chain of fp32 roundings a product x_k a_k goes through in the
+    library's low-rank rows bf16(sum_k x_k a_k). The matrix-core form gives
+    each of four waves whole slabs of 64*HS hidden columns (HS = 4 at ranks up
+    to 16, 2 at rank 32), so one wave sums at most min(hidden, ceil(ceil(hidden
+    / 64HS) / 4) * 64HS) products; every product is counted as its own rounding step (the
+    worst case for the matrix instruction's internal sum). The four waves'
+    partial sums then meet in three more additions. The block dot-product form
+    (a few rows) sums hidden/256 products per thread, six shuffle additions and
+    four wave partials, fewer steps. Nine covers the combining additions of
+    either form."""
+    def ceil_div(a, b):
+        return -(-a // b)
+    per_wave = max(min(hidden, 64 * hs * ceil_div(ceil_div(hidden, 64 * hs), 4)) for hs in (4, 2))
+    return per_wave + 9
+
+
+def lowrank_row_bound(ref: np.ndarray, x: np.ndarray, a: np.ndarray) -> np.ndarray:
+    """Elementwise bound on |row - X A| for a low-rank row stored by the
+    library (bf16 of an fp32 sum) against the exact float64 product ref = x @ a.
+    With k = lowrank_chain(hidden) and gamma_k = k u / (1 - k u), u = 2^-24,
+    the fp32 sum s of the exact products satisfies |s - ref| <= E =
+    gamma_k sum_k |x_k a_k| (the standard bound for summation with k rounding
+    steps on the longest path; products of two bf16 values are exact in fp32).
+    Rounding s to bf16 (nearest, unit roundoff 2^-8) adds at most
+    2^-8 |s| <= 2^-8 (|ref| + E), and 2^-8 |ref| is below one bf16 ulp of ref,
+    so |row - ref| <= ulp(ref) + (1 + 2^-8) E."""
+    k = lowrank_chain(x.shape[-1])
+    u = 2.0 ** -24
+    E = k * u / (1 - k * u) * (np.abs(x) @ np.abs(a))
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+    return ulp + (1 + 2.0 ** -8) * E
+
+
 def errors(got: np.ndarray, ref: np.ndarray):
     mask = ~np.isnan(ref[:, 0, 0])
     g, r = got[mask], ref[mask]

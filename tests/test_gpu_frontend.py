@@ -6,8 +6,9 @@ and the low-rank rows to its cache model. Bars:
   - q, and k, v as stored in the pages: within one bf16 ulp of the float64
     value (plus 1e-4 for fp32 summation), and the attention bar (max abs
     2e-2, relative L2 1e-2);
-  - low-rank rows: within one bf16 ulp of X A, plus 2^-20 sum_k |x_k a_k| for the
-    fp32 sum (which near a cancellation exceeds an ulp of the small result);
+  - low-rank rows: within one bf16 ulp of X A, plus the fp32 sum's error bound
+    gamma_k sum_k |x_k a_k| for the kernel's longest rounding chain k (which near a
+    cancellation exceeds an ulp of the small result);
   - page ids and lengths: exactly the oracle's;
   - attention over the projected cache: the attention bar.
 """
@@ -107,11 +108,11 @@ def run_case(shape, prefix, own_before, counts, theta, seed, with_a=True, attend
         if with_a:
             ai = a64[a] if shape.mode == BASE_SHARED else a64
             ref = x64[row:row + c] @ ai
-            # one bf16 ulp of the exact product, plus the fp32 summation's error,
-            # which near a cancellation (|X A| much below sum |x_k a_k|) can
-            # exceed an ulp of the small result
-            ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
-            bound = ulp + 2.0 ** -20 * (np.abs(x64[row:row + c]) @ np.abs(ai))
+            # one bf16 ulp of the exact product, plus the fp32 summation's error
+            # bound for the kernel's longest rounding chain, which near a
+            # cancellation (|X A| much below sum |x_k a_k|) can exceed an ulp
+            # of the small result
+            bound = R.lowrank_row_bound(ref, x64[row:row + c], ai)
             assert np.all(np.abs(got - ref) <= bound), ("lr", a, float(np.max(np.abs(got - ref) / bound)))
         else:
             assert np.all(got == 0), ("zero lr rows", a)

@@ -423,7 +423,12 @@ def test_lr_only_term():
 
 
 def test_lr_contribution_difference():
-    """The decode output with B_i minus the output with B_i = 0 matches the oracle's difference."""
+    """The decode output with B_i minus the output with B_i = 0 matches the
+    oracle's difference. This is the weaker check of the adapter term: each of
+    the two bf16 outputs carries its own rounding, about ten times the adapter
+    term's size, so the bar is 1e-2 of the difference plus that rounding floor.
+    The adapter term itself is held to rel-L2 1e-2 by the V_base = 0 tests
+    (test_lr_only_term, test_activation_offset_boundaries)."""
     import torch
     from lora_shared_kv_amd import skv as B
     R = _runner()
@@ -526,9 +531,10 @@ def test_lowrank_rows_at_slab_edges(hidden, rank, n):
     """The MFMA low-rank tiles (16 rows each; the hidden columns go to the four
     waves in slabs) at hidden sizes that end inside a slab or give some waves
     no slab, at every rank, with row counts around the tile edges. Each row is
-    within one bf16 ulp of the oracle's exact X A, plus the fp32 sum's error
-    (2^-20 sum |x_k a_k|, which near a cancellation exceeds an ulp of the
-    small result)."""
+    within one bf16 ulp of the oracle's exact X A plus the fp32 sum's error
+    bound gamma_k sum |x_k a_k| for the longest rounding chain k of the kernel
+    (gpu_runner.lowrank_row_bound; near a cancellation this term exceeds an
+    ulp of the small result)."""
     from lora_shared_kv_amd import skv as B
     R = _runner()
     shape = Shape("e", 1, 4, 2, 64, hidden, rank, 1, BASE_SHARED, 0)
@@ -541,10 +547,9 @@ def test_lowrank_rows_at_slab_edges(hidden, rank, n):
     ev = next(e for e in sc.events if isinstance(e, synth.AppendLowrank))
     ref = orc.lr[0][-1][0].get(n)
     got = bf16_bits_to_f64(np.stack([LRT[0, 0, pages[j // 64], :, j % 64] for j in range(n)]))
-    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
-    sum_err = 2.0 ** -20 * (np.abs(bf16_bits_to_f64(ev.x)) @ np.abs(bf16_bits_to_f64(ev.a)))
+    bound = R.lowrank_row_bound(ref, bf16_bits_to_f64(ev.x), bf16_bits_to_f64(ev.a))
     assert got.shape == (n, rank)
-    assert np.all(np.abs(got - ref) <= ulp + sum_err), np.max(np.abs(got - ref) / ulp)
+    assert np.all(np.abs(got - ref) <= bound), np.max(np.abs(got - ref) / bound)
 
 
 def test_decode_is_deterministic():
