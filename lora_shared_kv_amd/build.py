@@ -63,5 +63,28 @@ def build(verbose: bool = True) -> None:
         _run(cmd)
 
 
+ASAN_LIB = os.path.join(OUT, "libskv_host_asan.so")
+
+
+def build_asan(verbose: bool = True) -> str:
+    """The CPU build of the host runtime (null device backend) under
+    AddressSanitizer and UndefinedBehaviorSanitizer, for the sanitized runs of
+    the host-library tests; g++ only, no HIP code. Returns the library path.
+    Loading it needs the sanitizer runtimes preloaded (LD_PRELOAD)."""
+    os.makedirs(OUT, exist_ok=True)
+    cxx = shutil.which("g++") or "g++"
+    flags = ["-O1", "-g", "-std=c++17", "-fPIC", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+             "-fno-sanitize-recover=all", "-I" + INCLUDE, "-I" + CSRC]
+    cmd = [cxx] + flags + ["-shared", "-o", ASAN_LIB, os.path.join(CSRC, "runtime.cpp"),
+                           os.path.join(CSRC, "backend_null.cpp")]
+    if verbose:
+        print("[build] " + " ".join(os.path.basename(c) if i == 0 else c for i, c in enumerate(cmd)), flush=True)
+    _run(cmd)
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
-    build()
+    if len(sys.argv) > 1 and sys.argv[1] == "asan":
+        build_asan()
+    else:
+        build()

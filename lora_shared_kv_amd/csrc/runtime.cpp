@@ -16,6 +16,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <functional>
 #include <initializer_list>
 #include <set>
 #include <string>
@@ -173,7 +174,76 @@ void add_spans(const skv_ctx* c, std::vector<AppendJob>& jobs, const AppendJob& 
   }
 }
 
-int run_jobs(skv_ctx* c, const std::vector<AppendJob>& jobs) {
+// Bounds checks on what a launch will touch, run on the host before each
+// launch (no device traps): every page id inside the pool; every span's rows
+// inside the pages the job carries for it, those pages being the ones its
+// sequence's table holds (or will hold) at those positions. A failure is a
+// broken invariant of the store's metadata; the call fails before anything
+// is enqueued.
+using TableOf = std::function<const std::vector<int32_t>&(int slot)>;
+
+bool job_in_bounds(const skv_ctx* c, const AppendJob& j, const TableOf& table_of, char* msg, size_t cap) {
+  const Geometry& g = c->g;
+  if (j.n_spans < 0 || j.n_spans > skv::kMaxJobSpans || j.n_ids < 0 || j.n_ids > skv::kMaxJobPages) {
+    snprintf(msg, cap, "job with %d spans and %d page ids", j.n_spans, j.n_ids);
+    return false;
+  }
+  for (int i = 0; i < j.n_ids; ++i)
+    if (j.ids[i] < 0 || j.ids[i] >= g.max_pages) {
+      snprintf(msg, cap, "page id %d outside the pool of %d pages", j.ids[i], g.max_pages);
+      return false;
+    }
+  for (int s = 0; s < j.n_spans; ++s) {
+    const Span& sp = j.spans[s];
+    const bool ok = sp.seq_slot >= 0 && sp.seq_slot <= g.N && sp.pos0 >= 0 && sp.n > 0 && sp.src_row >= 0 &&
+                    sp.first_page == sp.pos0 / g.ps && sp.n_pages == ceil_div(sp.pos0 + sp.n, g.ps) - sp.first_page &&
+                    sp.ids_off >= 0 && sp.ids_off + sp.n_pages <= j.n_ids && sp.plane >= 0 && sp.plane < g.planes;
+    if (!ok) {
+      snprintf(msg, cap, "span %d (rows %d..%d of slot %d) does not fit its pages", s, sp.pos0, sp.pos0 + sp.n,
+               sp.seq_slot);
+      return false;
+    }
+    {
+      const std::vector<int32_t>& t = table_of(sp.seq_slot);
+      for (int i = 0; i < sp.n_pages; ++i)
+        if (sp.first_page + i >= (int)t.size() || t[sp.first_page + i] != j.ids[sp.ids_off + i]) {
+          snprintf(msg, cap, "span %d: page %d of slot %d is not the table's", s, sp.first_page + i, sp.seq_slot);
+          return false;
+        }
+    }
+  }
+  return true;
+}
+
+// Every page of each listed agent's view (shared pages below b, own pages
+// below S) is in its table and inside the pool.
+bool views_in_bounds(const skv_ctx* c, const AttnJob& job, char* msg, size_t cap) {
+  const Geometry& g = c->g;
+  const Layer& l = c->layers[job.layer];
+  for (int i = 0; i < job.n; ++i) {
+    const skv::AttnAgent& a = job.ag[i];
+    const std::vector<int32_t>* ts[2] = {&l.tbl[0], &l.tbl[1 + a.agent]};
+    const int need[2] = {ceil_div(a.b, g.ps), ceil_div(a.S, g.ps)};
+    for (int k = 0; k < 2; ++k) {
+      if ((int)ts[k]->size() < need[k]) {
+        snprintf(msg, cap, "agent %d: %d pages in its %s table, the view needs %d", a.agent, (int)ts[k]->size(),
+                 k ? "own" : "shared", need[k]);
+        return false;
+      }
+      for (int p = 0; p < need[k]; ++p)
+        if ((*ts[k])[p] < 0 || (*ts[k])[p] >= g.max_pages) {
+          snprintf(msg, cap, "agent %d: page id %d outside the pool", a.agent, (*ts[k])[p]);
+          return false;
+        }
+    }
+  }
+  return true;
+}
+
+int run_jobs(skv_ctx* c, const std::vector<AppendJob>& jobs, const TableOf& table_of) {
+  char msg[256];
+  for (auto& j : jobs)
+    if (!job_in_bounds(c, j, table_of, msg, sizeof msg)) return c->fail(SKV_ERR_STATE, "bounds check: %s", msg);
   for (auto& j : jobs) {
     int rc = skv::dev_append(c->g, j);
     if (rc != SKV_OK) return c->fail(rc, "device append failed: %s", skv::dev_last_error());
@@ -271,6 +341,16 @@ int plan_agent_rows(skv_ctx* c, int layer, int n, const int* agents, const int* 
     row += counts[i];
   }
   return SKV_OK;
+}
+
+// Table lookup for the bounds checks of a planned agent-row append: the
+// planned tables of the listed agents, the current ones of other sequences.
+TableOf planned_tables(const skv_ctx* c, int layer, int n, const int* agents, const AgentRows& ar) {
+  return [c, layer, n, agents, &ar](int s) -> const std::vector<int32_t>& {
+    for (int i = 0; i < n; ++i)
+      if (agents[i] + 1 == s) return ar.tables[i];
+    return c->layers[layer].tbl[s];
+  };
 }
 
 int finish_agent_rows(skv_ctx* c, int layer, int n, const int* agents, const int* counts, long total,
@@ -371,7 +451,7 @@ int skv_append_base(skv_ctx* c, int layer, int seq, int n, const skv_bf16* k, co
   proto.v = v;
   std::vector<AppendJob> jobs;
   add_spans(c, jobs, proto, table, slot, cur, n, 0, 0, nullptr);
-  int rc = run_jobs(c, jobs);
+  int rc = run_jobs(c, jobs, [&](int s) -> const std::vector<int32_t>& { return s == slot ? table : l.tbl[s]; });
   if (rc != SKV_OK) {
     for (int32_t p : taken) l.free.insert(p);
     return rc;
@@ -409,7 +489,7 @@ int skv_append_lowrank(skv_ctx* c, int layer, int seq, int plane, int n, const s
   proto.x = x;
   std::vector<AppendJob> jobs;
   add_spans(c, jobs, proto, l.tbl[slot], slot, cov, n, 0, plane, A);
-  int rc = run_jobs(c, jobs);
+  int rc = run_jobs(c, jobs, [&](int s) -> const std::vector<int32_t>& { return l.tbl[s]; });
   if (rc != SKV_OK) return rc;
   cov += n;
   (x ? c->counters.lr_rows : c->counters.lr_zero_rows) += n;
@@ -430,7 +510,7 @@ int skv_append_agents(skv_ctx* c, int layer, int n, const int* agents, const int
   AgentRows ar;
   rc = plan_agent_rows(c, layer, n, agents, counts, k, v, x, A, ar);
   if (rc != SKV_OK) return rc;
-  rc = run_jobs(c, ar.jobs);
+  rc = run_jobs(c, ar.jobs, planned_tables(c, layer, n, agents, ar));
   return finish_agent_rows(c, layer, n, agents, counts, total, x != nullptr, ar, rc);
 }
 
@@ -486,6 +566,7 @@ int skv_attn_prefill(skv_ctx* c, int layer, int n, const int* agents, const int*
   if (rc != SKV_OK) return rc;
   char msg[256];
   if ((rc = skv::plan_check_prefill(job, msg, sizeof msg)) != SKV_OK) return c->fail(rc, "%s", msg);
+  if (!views_in_bounds(c, job, msg, sizeof msg)) return c->fail(SKV_ERR_STATE, "bounds check: %s", msg);
   rc = skv::dev_attn_prefill(c->g, job);
   if (rc != SKV_OK) return c->fail(rc, "device prefill failed: %s", skv::dev_last_error());
   return SKV_OK;
@@ -499,6 +580,7 @@ int skv_attn_decode(skv_ctx* c, int layer, int n, const int* agents, const int* 
   if (rc != SKV_OK) return rc;
   char msg[256];
   if ((rc = skv::plan_check_decode(c->g, job, false, msg, sizeof msg)) != SKV_OK) return c->fail(rc, "%s", msg);
+  if (!views_in_bounds(c, job, msg, sizeof msg)) return c->fail(SKV_ERR_STATE, "bounds check: %s", msg);
   rc = skv::dev_attn_decode(c->g, job);
   if (rc != SKV_OK) return c->fail(rc, "device decode failed: %s", skv::dev_last_error());
   return SKV_OK;
@@ -594,6 +676,15 @@ static int decode_step(skv_ctx* c, int layer, int n, const int* agents, const in
   job.q = q;
   job.B = B;
   job.o = o;
+  const TableOf step_tables = [&](int s) -> const std::vector<int32_t>& {
+    for (int i = 0; i < n; ++i)
+      if (agents[i] + 1 == s) return tables[i];
+    return l.tbl[s];
+  };
+  if (!views_in_bounds(c, job, msg, sizeof msg) || !job_in_bounds(c, app, step_tables, msg, sizeof msg)) {
+    for (int32_t p : taken) l.free.insert(p);
+    return c->fail(SKV_ERR_STATE, "bounds check: %s", msg);
+  }
   rc = scratch_static ? skv::dev_decode_step_static(g, job, app) : skv::dev_decode_step(g, job, app);
   if (rc != SKV_OK) {
     for (int32_t p : taken) l.free.insert(p);
@@ -651,6 +742,14 @@ int skv_project_append(skv_ctx* c, int layer, int n, const int* agents, const in
   AgentRows ar;
   rc = plan_agent_rows(c, layer, n, agents, counts, nullptr, nullptr, A ? x : nullptr, A, ar);
   if (rc != SKV_OK) return rc;
+  {
+    char msg[256];
+    const TableOf tabs = planned_tables(c, layer, n, agents, ar);
+    for (const AppendJob& j : ar.jobs)
+      if (!job_in_bounds(c, j, tabs, msg, sizeof msg))
+        return finish_agent_rows(c, layer, n, agents, counts, total, A != nullptr, ar,
+                                 c->fail(SKV_ERR_STATE, "bounds check: %s", msg));
+  }
   for (const AppendJob& j : ar.jobs) {
     skv::ProjectJob pj{};
     pj.app = j;
