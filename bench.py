@@ -49,6 +49,9 @@ WORKLOADS = {
     "qwen2.5-1.5b-attn-8k": (28, 12, 2, 128, 1536, 16, 2, 0, 8192),
     "qwen3-1.7b-attn-8k": (28, 16, 8, 128, 2048, 16, 2, 0, 8192),
     "many-agent-28l-16k": (28, 16, 8, 128, 2048, 16, 8, 0, 16384),
+    # one GPU's shard of the headline when its 8 KV heads are split over 8 GPUs
+    # (one KV head, its 4 query heads; the low-rank rows and B_i columns of that head)
+    "llama3-8b-attn-32k-kvshard8": (32, 4, 1, 128, 4096, 8, 4, 1, 32768),
 }
 
 
@@ -276,6 +279,98 @@ def cpu_baseline(cfg, budget_s=15.0):
                                   f"(4 agents x {n_pre} tokens, view {view}), time scaled to all rows"}}
 
 
+def ttft_sweep(reps=5):
+    """Time to the first token of a new role, reusing the cached context versus
+    processing it again, on every layer of the attention path (appends,
+    prefill, one decode step), median of `reps` runs.
+
+    qwen3 shapes (28 layers, 16/8 heads, hidden 2048, rank 16), 8,192-token
+    base prefix with adapters off: a specialist takes over at b = 8192 - k and
+    recomputes the last k tokens with its adapter (k = 0: its first decode
+    token is its own), against the native path in which it processes all 8,192
+    tokens itself (paperlayer summary of arXiv 2609.17109, Sec. 3.1, Table 1).
+    qwen2.5 shapes (28 layers, 12/2 heads, hidden 1536, rank 16), shared context
+    of 1k-8k tokens: the next role computes only its 256-token turn over the
+    shared cache, against a per-role cache that must prefill the whole context
+    plus the turn (RoleKV, "Accomplishments that we're proud of": role-switch
+    first-token latency over the 1k-8k sweep)."""
+    import torch
+    from lora_shared_kv_amd import skv as B
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2025)
+
+    def randn(*shape, var=1.0):
+        t = torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32)
+        if var != 1.0:
+            t.mul_(var ** 0.5)
+        return t.to(torch.bfloat16)
+
+    def one(name, prefix, lr_prefix, b_new, n_new):
+        """Median ms of: agent 0 attached at b_new appends n_new own rows with its
+        adapter and prefills them on every layer, then one decode step."""
+        L, Hq, Hkv, d, hidden, r, N, mode, _ = WORKLOADS[name]
+        max_pages = prefix // 64 + (n_new + 2) // 64 + 8
+        cfg = dict(n_layers=L, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, hidden=hidden, rank=r, n_agents=N,
+                   mode=mode, page_size=64, max_pages=max_pages)
+        arena = torch.empty(B.skv_arena_bytes(cfg), dtype=torch.uint8, device=dev)
+        ctx = B.skv_create(cfg, arena)
+        A = randn(N, hidden, r, var=1.0 / hidden) if mode == 0 else randn(hidden, r, var=1.0 / hidden)
+        Bw = randn(N, r, Hkv * d, var=0.01 / r)
+        if b_new > 0:
+            for l in range(L):
+                for lo in range(0, prefix, 8192):
+                    n = min(8192, prefix - lo)
+                    B.skv_append_base(ctx, l, -1, randn(n, Hkv, d), randn(n, Hkv, d))
+                    for pl in (range(N) if mode == 0 else [0]):
+                        x = randn(n, hidden) if lr_prefix else None
+                        B.skv_append_lowrank(ctx, l, -1, pl, n, x, (A[pl].contiguous() if mode == 0 else A)
+                                             if lr_prefix else None)
+        kt, vt, xt, qt = (randn(max(n_new, 1), Hkv, d), randn(max(n_new, 1), Hkv, d),
+                          randn(max(n_new, 1), hidden), randn(max(n_new, 1), Hq, d))
+        ot = torch.empty_like(qt)
+        k1, v1, x1, q1 = randn(1, Hkv, d), randn(1, Hkv, d), randn(1, hidden), randn(1, Hq, d)
+        o1 = torch.empty_like(q1)
+        times = []
+        for rep in range(reps + 1):
+            B.skv_crop(ctx, 0, 0)
+            B.skv_crop(ctx, 0, b_new)
+            B.skv_sync(ctx)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for l in range(L):
+                for lo in range(0, n_new, 8192):
+                    n = min(8192, n_new - lo)
+                    B.skv_append_agents(ctx, l, [0], [n], kt[lo:lo + n], vt[lo:lo + n], xt[lo:lo + n], A)
+                if n_new:
+                    B.skv_attn_prefill(ctx, l, [0], [b_new], [n_new], [n_new], qt[:n_new], Bw, ot[:n_new])
+            for l in range(L):
+                B.skv_decode_step(ctx, l, [0], [b_new], [n_new], k1, v1, x1, A, q1, Bw, o1)
+            torch.cuda.synchronize()
+            if rep:  # the first run warms the kernels up
+                times.append(1e3 * (time.perf_counter() - t0))
+        B.skv_destroy(ctx)
+        del arena
+        times.sort()
+        return round(times[len(times) // 2], 3)
+
+    rows = []
+    P = 8192
+    native = one("qwen3-1.7b-attn-8k", 0, False, 0, P)
+    for k in (0, 160, 320):
+        reuse = one("qwen3-1.7b-attn-8k", P, False, P - k, k)
+        rows.append({"workload": "qwen3-1.7b-attn-8k", "context": P, "takeover_k": k, "reuse_ms": reuse,
+                     "native_ms": native, "ratio": round(native / reuse, 2)})
+    for P in (1024, 2048, 4096, 8192):
+        name = f"qwen2.5-1.5b-attn-{P // 1024}k"
+        reuse = one(name, P, True, P, 256)
+        reprefill = one(name, 0, True, 0, P + 256)
+        rows.append({"workload": name, "context": P, "turn_tokens": 256, "reuse_ms": reuse,
+                     "reprefill_ms": reprefill, "ratio": round(reprefill / reuse, 2)})
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -289,8 +384,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-events", action="store_true",
                     help="time the decode steps without per-launch HIP events (no roofline)")
-    ap.add_argument("--layout", default="shared", choices=["shared", "private"],
-                    help="shared: the prefix once, in SHARED pages (the method); private: every agent "
+    ap.add_argument("--layout", default="shared", choices=["shared", "private", "fullshared"],
+                    help="shared: the prefix once, in SHARED pages (the method); fullshared: the same pages, "
+                         "but every agent uses one full cache (no low-rank rows, no B_i: the pages' "
+                         "FullShared, which gives up the per-agent adapter term); private: every agent "
                          "holds its own copy of the prefix in its own pages (the Non-Shared comparison)")
     ap.add_argument("--adapters", default=None, choices=["BaseShared", "BaseLRShared"],
                     help="adapter mode instead of the workload's (BaseShared: one A_i per agent)")
@@ -304,6 +401,9 @@ def main():
                     help="time the fused front end (skv_project_append) on one layer of the workload: "
                          "one row per agent (a decode step) and 512 rows of one agent (a suffix) (the default)")
     ap.add_argument("--no-frontend", action="store_true", help="skip the front-end leg")
+    ap.add_argument("--ttft-sweep", action="store_true",
+                    help="only time the first token of a new role, reusing the cache versus re-prefilling it, "
+                         "at the qwen3 8K takeover shapes and the qwen2.5 1k-8k contexts; prints one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
     args = ap.parse_args()
@@ -311,6 +411,13 @@ def main():
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.ttft_sweep:
+        rows = ttft_sweep()
+        print(json.dumps({"metric": "time to first token after a role switch: cache reuse vs re-prefill "
+                                    "(attention path, all layers)", "unit": "ms", "higher_is_better": False,
+                          "n_gpus": 1, "data": "synthetic", "sweep": rows}), flush=True)
+        return
 
     import torch
     from lora_shared_kv_amd import skv as B
@@ -320,7 +427,10 @@ def main():
     if args.adapters:
         mode = 1 if args.adapters == "BaseLRShared" else 0
     private = args.layout == "private"
-    default_run = not private and mode == cfg[7]
+    fullshared = args.layout == "fullshared"
+    if fullshared:
+        mode = 1  # one plane, which holds zero rows
+    default_run = args.layout == "shared" and mode == cfg[7]
     G = Hq // Hkv
     total_steps = args.warmup + args.steps
     prefill_n = 512
@@ -345,6 +455,8 @@ def main():
     stream_gbs = B.skv_probe_stream_read(probe_buf, reps=5)
     del probe_buf
     mfma_tflops = B.skv_probe_mfma_bf16()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
 
     gen = torch.Generator(device=dev)
     gen.manual_seed(1003)
@@ -361,6 +473,8 @@ def main():
     A_of = (lambda a: A[a].contiguous()) if mode == 0 else (lambda a: A)
     plane_of = (lambda a: a) if mode == 0 else (lambda a: 0)
     Bw = randn(N, r, Hkv * d, var=0.01 / r)
+    if fullshared:
+        Bw.zero_()  # no per-agent adapter term
     chunk = 8192
     xbuf = randn(chunk, hidden)
     for l in range(L):
@@ -376,7 +490,10 @@ def main():
             else:
                 B.skv_append_base(ctx, l, -1, k_rows, v_rows)
                 for pl in (range(N) if mode == 0 else [0]):
-                    B.skv_append_lowrank(ctx, l, -1, pl, n, x_rows, A_of(pl))
+                    if fullshared:
+                        B.skv_append_lowrank(ctx, l, -1, pl, n, None, None)
+                    else:
+                        B.skv_append_lowrank(ctx, l, -1, pl, n, x_rows, A_of(pl))
     if not private:
         for a in range(N):
             B.skv_crop(ctx, a, prefix)
@@ -398,6 +515,8 @@ def main():
     # updates the suffix lengths it passes (and the library checks them).
     ptr = lambda ts: [t.data_ptr() for t in ts]
     kp, vp, xp, qp, op = ptr(kin), ptr(vin), ptr(xin), ptr(qin), ptr(out)
+    if fullshared:
+        xp = [0] * L  # zero low-rank rows for the new tokens too
     Ap, Bp = A.data_ptr(), Bw.data_ptr()
     ag = B.int_array(agents)
     ones = B.int_array([1] * N)
@@ -474,6 +593,10 @@ def main():
                     "kernel": split_kernel_name(d, N * G, N if mode == 0 else 1, r),
                     "algorithmic_bytes_per_launch": int(bytes_avg),
                     "avg_launch_us": round(avg_split_s * 1e6, 3)}
+    torch.cuda.synchronize()
+    memory["peak_allocated_bytes"] = int(torch.cuda.max_memory_allocated(dev))
+    memory["peak_note"] = ("torch allocator peak over setup and the decode steps: the arena (sized for this "
+                           "layout's pages) plus the per-layer inputs and outputs")
     per_kernel = {k: {"ms_total": round(v[0], 3), "launches": v[1],
                       "avg_us": round(1e3 * v[0] / max(v[1], 1), 3)} for k, v in times.items() if v[1]}
 

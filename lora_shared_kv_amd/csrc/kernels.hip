@@ -926,8 +926,12 @@ struct MergeParams {
 // LDS for the final product.
 constexpr int kMergeVec = 8;  // slots per thread held in registers
 
-template <int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
+// NT threads per row: 256, or 1024 when the row has more slots than 256
+// threads hold in one batch (few KV heads: many items per head), so that four
+// times the loads are in flight.
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void decode_merge_kernel(MergeParams p) {
+  constexpr int kGroups = NT / 32;  // slot groups at most (an element quad row has >= 17 quads)
   extern __shared__ __attribute__((aligned(16))) char s_app[];  // append blocks' staging
   if ((int)blockIdx.x >= p.n_rows) {
     // fused decode step: copy the new K/V rows into the pages; the rows merged
@@ -936,9 +940,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
     return;
   }
   __shared__ float s_w[kMaxMergeSlots];
-  __shared__ f32x4 s_red[8][40];
+  __shared__ f32x4 s_red[kGroups][40];
   __shared__ float s_v[128 + 32];
-  __shared__ float s_sm[16];  // maxima [4], sums [4], new score
+  __shared__ float s_sm[40];  // maxima [NT/64], sums [NT/64], new score
   __shared__ u32x4 s_b[32 * 128 / 8];  // B_i slice [r][D] bf16
   const int row_id = blockIdx.x;
   const int hh = row_id % p.G;
@@ -953,7 +957,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
   const int ts = max(min(t, I - 1), 0);
   float m_ld = 0.f, l_ld = 0.f;
   const int NQ = E / 4;
-  const int NG = min(8, (int)blockDim.x / NQ);
+  const int NG = min(kGroups, NT / NQ);
   const int qd = t % NQ, sg = min(t / NQ, NG - 1);
   const bool quad_thread = t < NQ * NG;
   f32x4 vals[kMergeVec];
@@ -967,10 +971,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
   const int HD = p.Hkv * D;
   constexpr int BV = D / 8;  // 16-byte vectors per B_i row slice
   const u16* bsl = p.B + (uint64_t)p.ag_id[a] * r * HD + g * D;
-  u32x4 bvec[2];
+  constexpr int NBV = (32 * BV + NT - 1) / NT;  // B_i vectors per thread (rank up to 32)
+  u32x4 bvec[NBV];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int v = min(t + 256 * i, r * BV - 1);
+  for (int i = 0; i < NBV; ++i) {
+    const int v = min(t + NT * i, r * BV - 1);
     bvec[i] = *reinterpret_cast<const u32x4*>(bsl + (uint64_t)(v / BV) * HD + 8 * (v % BV));
   }
   float dot = 0.f, nv = 0.f;
@@ -990,19 +995,22 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
     nv = t < D ? vv : (t < E && p.new_lr_on[a] ? lv : 0.f);
   }
   // --- softmax statistics
+  constexpr int NWV = NT / 64;  // waves
   const float m_s = t < I ? m_ld : -1e30f, l_s = t < I ? l_ld : 0.f;
   float M = wave_max(m_s);
   if (p.step && w == 0) {
     dot = wave_sum(dot);
-    if (lane == 0) s_sm[8] = dot * p.scale_log2;
+    if (lane == 0) s_sm[2 * NWV] = dot * p.scale_log2;
   }
   if (lane == 0) s_sm[w] = M;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-    if (t + 256 * i < r * BV) s_b[t + 256 * i] = bvec[i];
+  for (int i = 0; i < NBV; ++i)
+    if (t + NT * i < r * BV) s_b[t + NT * i] = bvec[i];
   __syncthreads();
-  const float m_new = p.step ? s_sm[8] : -1e30f;
-  M = fmaxf(fmaxf(fmaxf(s_sm[0], s_sm[1]), fmaxf(s_sm[2], s_sm[3])), m_new);
+  const float m_new = p.step ? s_sm[2 * NWV] : -1e30f;
+  M = m_new;
+#pragma unroll
+  for (int i = 0; i < NWV; ++i) M = fmaxf(M, s_sm[i]);
   // slots beyond the first blockDim.x are folded in below through s_w
   const float e_s = t < I ? __builtin_amdgcn_exp2f(m_s - M) : 0.f;
   if (t < I) s_w[t] = e_s;
@@ -1013,10 +1021,13 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
     L += e * slot_row(s)[E + 1];
   }
   L = wave_sum(L);
-  if (lane == 0) s_sm[4 + w] = L;
+  if (lane == 0) s_sm[NWV + w] = L;
   __syncthreads();
   const float e_new = p.step ? __builtin_amdgcn_exp2f(m_new - M) : 0.f;
-  const float inv = 1.f / (s_sm[4] + s_sm[5] + s_sm[6] + s_sm[7] + e_new);
+  float den = e_new;
+#pragma unroll
+  for (int i = 0; i < NWV; ++i) den += s_sm[NWV + i];
+  const float inv = 1.f / den;
   // --- weighted sums: element quads x slot groups
   if (quad_thread) {
     f32x4 acc = {0, 0, 0, 0};
@@ -2432,8 +2443,15 @@ static int decode_impl(const Geometry& g, const AttnJob& job, const AppendJob* a
     mp.n_rows = n * g.Hkv * g.G;
     const size_t mlds = mp.n_app ? (size_t)64 * (128 + 8) * 2 : 0;
     const int kind = timed ? 3 : -1;
-    rc = g.D == 128 ? launch(g, kind, decode_merge_kernel<128>, dim3(mp.n_rows + mp.n_app), mlds, mp, "decode_merge_kernel")
-                    : launch(g, kind, decode_merge_kernel<64>, dim3(mp.n_rows + mp.n_app), mlds, mp, "decode_merge_kernel");
+    // a row's slots beyond what 256 threads hold in one batch: 1024 threads per row
+    const bool wide = items_per_head > kMergeVec * std::min(8, 256 / ((g.D + g.r) / 4));
+    const dim3 mgrid(mp.n_rows + mp.n_app);
+    if (g.D == 128)
+      rc = wide ? launch(g, kind, decode_merge_kernel<128, 1024>, mgrid, mlds, mp, "decode_merge_kernel", 1024)
+                : launch(g, kind, decode_merge_kernel<128, 256>, mgrid, mlds, mp, "decode_merge_kernel");
+    else
+      rc = wide ? launch(g, kind, decode_merge_kernel<64, 1024>, mgrid, mlds, mp, "decode_merge_kernel", 1024)
+                : launch(g, kind, decode_merge_kernel<64, 256>, mgrid, mlds, mp, "decode_merge_kernel");
     if (rc != SKV_OK) return rc;
   }
   return SKV_OK;

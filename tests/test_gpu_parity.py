@@ -173,6 +173,28 @@ def test_llama3_long_prefix_decode(prefix, steps):
     R.run_parity(sc, log=log)
 
 
+def test_llama3_kv_head_shard():
+    """One GPU's share of the headline under KV-head sharding over 8 GPUs: one
+    KV head and its 4 query heads (the 4 agents' 16 stacked rows unchanged),
+    the shared A's low-rank rows and B_i's columns of that head: a 512-token
+    suffix prefill per agent and fused decode steps over a 32,768-token shared
+    prefix, every row."""
+    R = _runner()
+    shape = synth.LLAMA3.with_(n_q_heads=4, n_kv_heads=1, prefix=32768)
+    sc = synth.Schedule(shape, 1031, n_layers=1)
+    sc.draw_adapters()
+    sc.shared_prefix(32768)
+    agents = list(range(shape.n_agents))
+    for a in agents:
+        sc.attach(a)
+    sc.own_rows(0, agents, [512] * 4)
+    sc.attend("prefill", 0, agents, [512] * 4, tag="shard prefill")
+    for t in range(3):
+        sc.decode_step(0, agents, tag=f"shard step {t}")
+    _, _, res = R.run_parity(sc, log=log)
+    assert len(res) == 4
+
+
 def test_many_agent_mixed_turns():
     """All six turns of the many-agent workload (one layer): four agents
     prefill 512 own tokens while four decode, then the lead agent crops 256
