@@ -1865,10 +1865,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SK ? 1 : 2,
   constexpr int kWaitStage = (kAfter & 15) | ((kAfter >> 4) << 14) | (7 << 4) | (15 << 8);
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) issue(s);
+  // copies one wave issues per stage (its X share and its W fragments)
+  constexpr int XPWC = SK ? NF : (NF >= 4 ? NF / 4 : 1);
+  constexpr int NCOPY = XPWC + 2 * NJ;
+  constexpr int NMF = 2 * NJ * NC;  // MFMAs per wave and stage
   for (int s = 0; s < kcnt; ++s) {
     __builtin_amdgcn_s_waitcnt(kWaitStage);
     if (!SK) __syncthreads();  // SK: every wave reads only its own ring
-    issue(s + NS - 1);
+    if (SK) issue(s + NS - 1);
     const u16* slot = ring + (s % NS) * SLOT;
     bf16x8 bx[2][NC], aw[2][NJ];
 #pragma unroll
@@ -1880,6 +1884,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SK ? 1 : 2,
 #pragma unroll
       for (int c = 0; c < NC; ++c) bx[ks][c] = *reinterpret_cast<const bf16x8*>(slot + (2 * c + ks) * 512 + lane * 8);
     }
+    // the next stage's copies go into the slot read for the last time before
+    // the barrier above (the split form issued them ahead of its reads)
+    if (!SK) issue(s + NS - 1);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -1888,9 +1895,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SK ? 1 : 2,
         for (int c = 0; c < NC; ++c)
           acc[c][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[ks][jj], bx[ks][c], acc[c][jj], 0, 0, 0);
     // every LDS read of the stage first, then the MFMAs (the first ones wait
-    // only for their own operands)
+    // only for their own operands); in the row-tile form the next stage's
+    // copies are spread among the MFMAs, so that their issue (the CU moves 64
+    // bytes of them a clock) runs under the matrix work instead of ahead of it
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * NJ + 2 * NC, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NJ * NC, 0);
+    if constexpr (SK) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+    } else {
+      constexpr int kPer = NMF / NCOPY > 0 ? NMF / NCOPY : 1;
+#pragma unroll
+      for (int i = 0; i < NCOPY; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kPer, 0);
+      }
+      if (NMF > kPer * NCOPY) __builtin_amdgcn_sched_group_barrier(0x008, NMF - kPer * NCOPY, 0);
+    }
   }
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): no copy outlives the wave
   if constexpr (SK) {
