@@ -106,12 +106,19 @@ def project_bytes(Hq, Hkv, d, hidden, r, rows, planes):
 
 
 def project_kernel_name(Hq, Hkv, d, rows):
-    """Template arguments the library picks for a front-end call of one job:
-    the split form up to 16 rows, else 32-row tiles while 64-row tiles would
-    give fewer workgroups than the 256 CUs, else 64-row tiles."""
-    groups = ((Hq + 2 * Hkv) * d // 64 + 3) // 4
-    tm = 16 if rows <= 16 else (32 if groups * ((rows + 63) // 64) < 256 else 64)
-    return f"project_kernel<{d},{tm},{'true' if tm == 16 else 'false'}>"
+    """Template arguments the library picks for a front-end call of one
+    agent's rows: the split form up to 16 rows, else 128-token tiles of three
+    or four half units, whichever gives fewer rounds of workgroups over the
+    256 CUs (the low-rank blocks included) times bytes per tile."""
+    if rows <= 16:
+        return f"project_split_kernel<{d}>"
+    units = (Hq + 2 * Hkv) * d // 64
+    tiles = -(-rows // 128)
+    app = -(-rows // 16) if rows > 8 else rows
+    t4 = -(-2 * units // 4) * tiles + app
+    t3 = -(-2 * units // 3) * tiles + app
+    nh = 3 if -(-t3 // 256) * 7 < -(-t4 // 256) * 8 else 4
+    return f"project_wide_kernel<{d},4,{nh}>"
 
 
 def frontend_timing(B, cfg, randn, reps=20):

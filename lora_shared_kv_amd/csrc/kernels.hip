@@ -210,7 +210,7 @@ struct AppendParams {
 
 constexpr int kLrTile = 16;  // rows per MFMA low-rank block
 
-template <int D>
+template <int D, int NTA>
 __device__ void append_kv_tile(const AppendParams& p, int s, int blk, char* smem) {
   const skv::Span& sp = p.spans[s];
   const int pi = blk / p.Hkv, h = blk % p.Hkv;
@@ -224,7 +224,7 @@ __device__ void append_kv_tile(const AppendParams& p, int s, int blk, char* smem
   constexpr int VPR = D / 8;  // 16-byte vectors per row
   // K: eight consecutive d of one key stay contiguous in the tile
   u16* kdst = p.K + ((uint64_t)page * p.Hkv + h) * kPage * D;
-  for (int i = threadIdx.x; i < rows * VPR; i += blockDim.x) {
+  for (int i = threadIdx.x; i < rows * VPR; i += NTA) {
     const int rr = i / VPR, c = i % VPR;
     const u16* src = p.k + ((uint64_t)(src0 + rr) * p.Hkv + h) * D + c * 8;
     *reinterpret_cast<u32x4*>(kdst + k_tile_off<D>(lo + rr, c * 8)) = *reinterpret_cast<const u32x4*>(src);
@@ -233,7 +233,7 @@ __device__ void append_kv_tile(const AppendParams& p, int s, int blk, char* smem
   // LDS, then write whole 8-key groups as vectors and partial groups by element
   u16* vs = reinterpret_cast<u16*>(smem);  // [64][D + 8]
   constexpr int ld = D + 8;
-  for (int i = threadIdx.x; i < rows * VPR; i += blockDim.x) {
+  for (int i = threadIdx.x; i < rows * VPR; i += NTA) {
     const int rr = i / VPR, c = i % VPR;
     const u16* src = p.v + ((uint64_t)(src0 + rr) * p.Hkv + h) * D + c * 8;
     const u32x4 val = *reinterpret_cast<const u32x4*>(src);
@@ -244,7 +244,7 @@ __device__ void append_kv_tile(const AppendParams& p, int s, int blk, char* smem
   __syncthreads();
   u16* vdst = p.VT + ((uint64_t)page * p.Hkv + h) * D * kPage;
   const int g0 = lo >> 3, g1 = (hi + 7) >> 3;  // 8-key groups touched
-  for (int i = threadIdx.x; i < (g1 - g0) * D; i += blockDim.x) {
+  for (int i = threadIdx.x; i < (g1 - g0) * D; i += NTA) {
     const int grp = g0 + i / D, d = i % D;
     const int k0 = grp * 8;
     if (k0 >= lo && k0 + 8 <= hi) {
@@ -259,13 +259,15 @@ __device__ void append_kv_tile(const AppendParams& p, int s, int blk, char* smem
   }
 }
 
+template <int NTA>
 __device__ void append_kv_block(const AppendParams& p, int s, int blk, char* smem) {
   if (p.D == 128)
-    append_kv_tile<128>(p, s, blk, smem);
+    append_kv_tile<128, NTA>(p, s, blk, smem);
   else
-    append_kv_tile<64>(p, s, blk, smem);
+    append_kv_tile<64, NTA>(p, s, blk, smem);
 }
 
+template <int NTA>
 __device__ void append_lr_zero_block(const AppendParams& p, int s, int pi) {
   const skv::Span& sp = p.spans[s];
   const int page_idx = sp.first_page + pi;
@@ -275,7 +277,7 @@ __device__ void append_lr_zero_block(const AppendParams& p, int s, int pi) {
   const int hi = (page_idx == (end - 1) / kPage) ? (end - 1) % kPage + 1 : kPage;
   u16* dst = p.LRT + sp.plane * p.lr_plane + (uint64_t)page * p.r * kPage;
   const int rows = hi - lo;
-  for (int i = threadIdx.x; i < p.r * rows; i += blockDim.x) {
+  for (int i = threadIdx.x; i < p.r * rows; i += NTA) {
     int k = i / rows, rr = i % rows;
     dst[k * kPage + lo + rr] = 0;
   }
@@ -285,7 +287,7 @@ __device__ void append_lr_zero_block(const AppendParams& p, int s, int pi) {
 // decode step appends one row per agent). Each thread takes 8 consecutive
 // hidden columns at a time with 16-byte loads of x and of the matching A rows,
 // so all of a thread's loads are independent and in flight together.
-template <int R>
+template <int R, int NTA>
 __device__ void append_lr_dot_rows(const AppendParams& p, int s, int row, char* smem) {
   const skv::Span& sp = p.spans[s];
   const int H = p.hidden;
@@ -295,7 +297,7 @@ __device__ void append_lr_dot_rows(const AppendParams& p, int s, int row, char* 
 #pragma unroll
   for (int k = 0; k < R; ++k) acc[k] = 0.f;
 #pragma unroll 2
-  for (int u8 = threadIdx.x; u8 < H / 8; u8 += blockDim.x) {
+  for (int u8 = threadIdx.x; u8 < H / 8; u8 += NTA) {
     const u32x4 xv = *reinterpret_cast<const u32x4*>(x + u8 * 8);
     const u16* arow = sp.a + (uint64_t)u8 * 8 * R;
     u32x4 av[8][VR];
@@ -334,19 +336,20 @@ __device__ void append_lr_dot_rows(const AppendParams& p, int s, int row, char* 
   if (threadIdx.x < R) {
     const int k = threadIdx.x;
     float v = 0.f;
-    for (int ww = 0; ww < (int)(blockDim.x >> 6); ++ww) v += red[ww * R + k];
+    for (int ww = 0; ww < NTA / 64; ++ww) v += red[ww * R + k];
     const int pos = sp.pos0 + row;
     const int page = p.ids[sp.ids_off + pos / kPage - sp.first_page];
     p.LRT[sp.plane * p.lr_plane + (uint64_t)page * R * kPage + k * kPage + pos % kPage] = f2bf(v);
   }
 }
 
+template <int NTA>
 __device__ void append_lr_dot_block(const AppendParams& p, int s, int row, char* smem) {
   switch (p.r) {
-    case 4: append_lr_dot_rows<4>(p, s, row, smem); break;
-    case 8: append_lr_dot_rows<8>(p, s, row, smem); break;
-    case 16: append_lr_dot_rows<16>(p, s, row, smem); break;
-    default: append_lr_dot_rows<32>(p, s, row, smem); break;
+    case 4: append_lr_dot_rows<4, NTA>(p, s, row, smem); break;
+    case 8: append_lr_dot_rows<8, NTA>(p, s, row, smem); break;
+    case 16: append_lr_dot_rows<16, NTA>(p, s, row, smem); break;
+    default: append_lr_dot_rows<32, NTA>(p, s, row, smem); break;
   }
 }
 
@@ -493,14 +496,16 @@ __device__ void append_lr_mfma_block(const AppendParams& p, int s, int tile, cha
 // entries). smem must hold at least 64 * (128 + 8) bf16. KV and MFMA_LR say
 // whether the kernel carries the K/V tile copies and the MFMA low-rank tiles:
 // launches whose jobs never hold such blocks leave that code out, which keeps
-// them small (the host checks the jobs it gives them).
-template <bool KV = true, bool MFMA_LR = true>
+// them small (the host checks the jobs it gives them). NTA threads of the
+// block run it (the first NTA; the MFMA low-rank tiles take four waves).
+template <bool KV = true, bool MFMA_LR = true, int NTA = 256>
 __device__ void append_block(const AppendParams& p, int b, char* smem) {
+  static_assert(!MFMA_LR || NTA == 256, "the MFMA low-rank tiles are written for four waves");
   if (b == 0 && p.update_tables) {
     for (int s = 0; s < p.n_spans; ++s) {
       const skv::Span& sp = p.spans[s];
       int32_t* t = p.tbl + sp.seq_slot * p.tbl_seq + sp.first_page;
-      for (int i = threadIdx.x; i < sp.n_pages; i += blockDim.x) t[i] = p.ids[sp.ids_off + i];
+      for (int i = threadIdx.x; i < sp.n_pages; i += NTA) t[i] = p.ids[sp.ids_off + i];
     }
   }
   const int n_kv = p.kv_block0[p.n_spans];
@@ -509,7 +514,7 @@ __device__ void append_block(const AppendParams& p, int b, char* smem) {
     if constexpr (KV) {
       int s = 0;
       while (b >= p.kv_block0[s + 1]) ++s;
-      append_kv_block(p, s, b - p.kv_block0[s], smem);
+      append_kv_block<NTA>(p, s, b - p.kv_block0[s], smem);
     }
     return;
   }
@@ -518,9 +523,9 @@ __device__ void append_block(const AppendParams& p, int b, char* smem) {
   while (b >= p.lr_block0[s + 1]) ++s;
   const int sub = b - p.lr_block0[s];
   if (p.lr_kind[s] == 0)
-    append_lr_zero_block(p, s, sub);
+    append_lr_zero_block<NTA>(p, s, sub);
   else if (p.lr_kind[s] == 1)
-    append_lr_dot_block(p, s, sub, smem);
+    append_lr_dot_block<NTA>(p, s, sub, smem);
   else if constexpr (MFMA_LR) {
     if (p.r == 4)
       append_lr_mfma_block<0, 4>(p, s, sub, smem);
@@ -936,7 +941,7 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(MergeParams p) {
   if ((int)blockIdx.x >= p.n_rows) {
     // fused decode step: copy the new K/V rows into the pages; the rows merged
     // here take the new token from the step's inputs instead
-    append_block<true, false>(p.app, blockIdx.x - p.n_rows, s_app);
+    append_block<true, false, NT>(p.app, blockIdx.x - p.n_rows, s_app);
     return;
   }
   __shared__ float s_w[kMaxMergeSlots];
@@ -1763,180 +1768,23 @@ struct ProjectParams {
 };
 static_assert(sizeof(ProjectParams) <= 4096, "kernel arguments");
 
-// Ring slots of the projection: the split form keeps two stages in flight
-// ahead of the MFMAs (three slots); the 64-row form keeps one (two slots,
-// 80 KB) so that two workgroups share a CU and one's copies overlap the other's
-// MFMAs (measured 20% faster from 1,024 rows on, equal below).
-constexpr int project_slots(bool sk) { return sk ? 3 : 2; }
-
-// SK (split K, for few rows): a workgroup takes half a unit (one rotary-paired
-// pair of 16-feature tiles) and one 16-row tile, and its four waves take a
-// quarter of the hidden columns each, with rings of their own; the partial
-// sums meet in LDS at the end. Eight times as many workgroups stream W as with
-// four units per workgroup: the weight stream of a few rows is bound by how
-// many CUs pull on it.
-template <int D, int TM, bool SK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SK ? 1 : 2, SK ? 1 : 2))) void project_kernel(
-    ProjectParams p) {
-  static_assert(!SK || TM == 16, "the split form takes 16-row tiles");
-  constexpr int NC = TM / 16;           // 16-token tiles
-  constexpr int NF = 2 * NC;            // X fragments (16 tokens x 32 columns) per 64-column stage
-  constexpr int NS = project_slots(SK);
-  constexpr int NJ = SK ? 2 : 4;  // 16-feature tiles per wave
-  // u16 per ring slot: X fragments, then 2 NJ W fragments per wave (SK: one wave's ring)
-  constexpr int SLOT = (NF + (SK ? 2 * NJ : 8 * NJ)) * 512;
-  constexpr int RING = (SK ? 4 : 1) * NS * SLOT * 2;
-  static_assert(RING >= 64 * (128 + 8) * 2, "the low-rank blocks stage rows in the same LDS");
-  extern __shared__ __attribute__((aligned(16))) u16 s_pr[];
-  const int b = blockIdx.x;
-  if (b >= 8 * p.per_xcd) {
-    append_block(p.app, b - 8 * p.per_xcd, reinterpret_cast<char*>(s_pr));
-    return;
-  }
-  // Block b runs on XCD b % 8: each XCD takes a contiguous run of tiles, token
-  // tile fastest, so the token tiles of one unit group read W through one L2.
-  const int lb = (b % 8) * p.per_xcd + b / 8;
-  if (lb >= p.n_gemm) return;
-  const int ug = lb / p.tok_tiles, tt = lb % p.tok_tiles;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+// Epilogue of the projection for one wave: C tiles acc[c][jj] hold 16-token
+// tile c (tokens t0 + 16 c + n) and feature tile jj of unit hu of head `head`;
+// tiles jj and jj + NJ/2 are the two members of the rotary pairs (feature
+// tiles jp and jp + 2 of the unit: jp = pp, or `half` when a wave holds half a
+// unit). Rotates q and k, writes q to the caller's rows and k, v into their
+// pages in the K / V^T tile order (bf16, round to nearest even).
+template <int D, int NC, int NJ>
+__device__ __forceinline__ void project_epilogue(const ProjectParams& p, const f32x4 (&acc)[NC][NJ], int t0,
+                                                 int head, int hu, int half) {
+  const int lane = threadIdx.x & 63;
   const int n = lane & 15, qd = lane >> 4;
-  const int unit = SK ? ug / 2 : ug * 4 + wave;
-  const int half = SK ? ug % 2 : 0;  // SK: feature tiles half and half + 2 of the unit
-  const bool active = unit < p.n_units;
-  constexpr int UPH = D / 64;  // units per head
-  const int uc = active ? unit : p.n_units - 1;
-  const int head = uc / UPH, hu = uc % UPH;
-  const int H = p.hidden, nk = H / 64;
-  const int kbeg = SK ? wave * nk / 4 : 0;                // this wave's stages [kbeg, kbeg + kcnt)
-  const int kcnt = SK ? (wave + 1) * nk / 4 - kbeg : nk;
-  u16* const ring = s_pr + (SK ? wave * NS * SLOT : 0);
-  // W is packed (pack_qkv_kernel): the unit's eight fragments of a stage are
-  // 8 KB of contiguous memory, so each copy is 1 KB contiguous and a wave
-  // streams its unit's weights front to back.
-  const __amdgpu_buffer_rsrc_t wr = byte_rsrc(p.w + (uint64_t)uc * nk * 8 * 512, nk * 8 * 1024);
-  // X fragment (c, ks): lane (n, qd) copies token 16 c + n, columns 32 ks + 8 qd + [0, 8).
-  // Rows past the job read as zero (buffer bounds).
-  const __amdgpu_buffer_rsrc_t xr = byte_rsrc(p.x + (uint64_t)p.row0 * H, p.rows * H * 2);
-  const int xoff0 = ((tt * TM + n) * H + 8 * qd) * 2;
-
-  // tile jj of the wave is feature tile j = jj (four per wave) or half + 2 jj (SK)
-  f32x4 acc[NC][NJ];
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-#pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) acc[c][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Copies of stage s into ring slot s % NS: this wave's share of the X
-  // fragments, then its own eight W fragments. Stages past the end copy the
-  // last one again, so every stage issues the same copies and the wait below
-  // holds.
-  auto issue = [&](int s) {
-    if (kcnt == 0) return;
-    const int sc = kbeg + (s < kcnt ? s : kcnt - 1);
-    u16* slot = ring + (s % NS) * SLOT;
-    // X fragments per wave: SK all of them; otherwise a quarter (NF < 4:
-    // waves 0 .. NF-1 take one)
-    constexpr int XPW = SK ? NF : (NF >= 4 ? NF / 4 : 1);
-    static_assert(SK || NF < 4 || NF % 4 == 0, "X fragments split evenly over the waves");
-#pragma unroll
-    for (int i = 0; i < XPW; ++i) {
-      const int fi = SK ? i : wave + 4 * i;
-      if (!SK && NF < 4 && fi >= NF) break;
-      const int c = fi >> 1, ks = fi & 1;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (void __attribute__((address_space(3)))*)(slot + fi * 512), 16,
-                                               xoff0 + (16 * c * H + 64 * sc + 32 * ks) * 2, 0, 0, 0);
-    }
-    u16* wdst = slot + (NF + (SK ? 0 : 2 * NJ * wave)) * 512;
-#pragma unroll
-    for (int jj = 0; jj < NJ; ++jj)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int j = SK ? half + 2 * jj : jj;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (void __attribute__((address_space(3)))*)(wdst + (2 * jj + ks) * 512),
-                                                 16, ((sc * 8 + 2 * j + ks) * 64 + lane) * 16, 0, 0, 0);
-      }
-  };
-  // Before stage s: stages s .. s + NS - 2 are in flight (their X copies, then
-  // 8 W copies each); with no more than NS - 2 stages' worth outstanding, all
-  // of stage s's copies have landed (when the waves' X shares differ, 8 per
-  // stage is the smaller count). The barrier publishes every wave's X copies
-  // and retires the reads of the slot the next issue overwrites.
-  constexpr int kAfter = (NS - 2) * (SK ? NF + 2 * NJ : (NF % 4 == 0 ? 2 * NJ + NF / 4 : 2 * NJ));
-  constexpr int kWaitStage = (kAfter & 15) | ((kAfter >> 4) << 14) | (7 << 4) | (15 << 8);
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s) issue(s);
-  // copies one wave issues per stage (its X share and its W fragments)
-  constexpr int XPWC = SK ? NF : (NF >= 4 ? NF / 4 : 1);
-  constexpr int NCOPY = XPWC + 2 * NJ;
-  constexpr int NMF = 2 * NJ * NC;  // MFMAs per wave and stage
-  for (int s = 0; s < kcnt; ++s) {
-    __builtin_amdgcn_s_waitcnt(kWaitStage);
-    if (!SK) __syncthreads();  // SK: every wave reads only its own ring
-    if (SK) issue(s + NS - 1);
-    const u16* slot = ring + (s % NS) * SLOT;
-    bf16x8 bx[2][NC], aw[2][NJ];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int jj = 0; jj < NJ; ++jj)
-        aw[ks][jj] =
-            *reinterpret_cast<const bf16x8*>(slot + (NF + (SK ? 0 : 2 * NJ * wave) + 2 * jj + ks) * 512 + lane * 8);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) bx[ks][c] = *reinterpret_cast<const bf16x8*>(slot + (2 * c + ks) * 512 + lane * 8);
-    }
-    // the next stage's copies go into the slot read for the last time before
-    // the barrier above (the split form issued them ahead of its reads)
-    if (!SK) issue(s + NS - 1);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int jj = 0; jj < NJ; ++jj)
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-          acc[c][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[ks][jj], bx[ks][c], acc[c][jj], 0, 0, 0);
-    // every LDS read of the stage first, then the MFMAs (the first ones wait
-    // only for their own operands); in the row-tile form the next stage's
-    // copies are spread among the MFMAs, so that their issue (the CU moves 64
-    // bytes of them a clock) runs under the matrix work instead of ahead of it
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NJ + 2 * NC, 0);
-    if constexpr (SK) {
-      __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
-    } else {
-      constexpr int kPer = NMF / NCOPY > 0 ? NMF / NCOPY : 1;
-#pragma unroll
-      for (int i = 0; i < NCOPY; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, kPer, 0);
-      }
-      if (NMF > kPer * NCOPY) __builtin_amdgcn_sched_group_barrier(0x008, NMF - kPer * NCOPY, 0);
-    }
-  }
-  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): no copy outlives the wave
-  if constexpr (SK) {
-    // waves 1..3 hand their partial sums to wave 0 (added in wave order)
-    __syncthreads();  // every wave is done with its ring
-    float* red = reinterpret_cast<float*>(s_pr);  // [3][64 lanes][4 NJ]
-    if (wave > 0) {
-#pragma unroll
-      for (int jj = 0; jj < NJ; ++jj)
-        *reinterpret_cast<f32x4*>(red + ((wave - 1) * 64 + lane) * 4 * NJ + 4 * jj) = acc[0][jj];
-    }
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int w = 0; w < 3; ++w)
-#pragma unroll
-      for (int jj = 0; jj < NJ; ++jj)
-        acc[0][jj] += *reinterpret_cast<const f32x4*>(red + (w * 64 + lane) * 4 * NJ + 4 * jj);
-  }
-  if (!active) return;
-
   const int part = head < p.Hq ? 0 : (head < p.Hq + p.Hkv ? 1 : 2);  // q, k, v
   const int hh = part == 0 ? head : (part == 1 ? head - p.Hq : head - p.Hq - p.Hkv);
   constexpr double kTwoPi = 6.283185307179586;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const int t = tt * TM + 16 * c + n;
+    const int t = t0 + 16 * c + n;
     if (t >= p.rows) continue;
     const int row = p.row0 + t;
     int s = 0;
@@ -1949,7 +1797,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SK ? 1 : 2,
 #pragma unroll
     for (int pp = 0; pp < NJ / 2; ++pp) {
       // rotary pair: tiles jj = pp and pp + NJ/2 are feature tiles jp and jp + 2
-      const int jp = SK ? half : pp;
+      const int jp = NJ == 2 ? half : pp;
       const int dlo = 32 * hu + 16 * jp + 4 * qd;  // element 0 of the low half; the high half is + D/2
       float lo[4], hi[4];
 #pragma unroll
@@ -1996,6 +1844,288 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SK ? 1 : 2,
       }
     }
   }
+}
+
+
+// Few rows (a decode step, up to 16): split K. A workgroup takes half a unit
+// (one rotary-paired pair of 16-feature tiles) and the 16-row tile, and its
+// four waves take a quarter of the hidden columns each, with rings of three
+// slots of their own (two stages in flight ahead of the MFMAs); the partial
+// sums meet in LDS at the end. Eight times as many workgroups stream W as with
+// four units per workgroup: the weight stream of a few rows is bound by how
+// many CUs pull on it.
+constexpr int kSplitSlots = 3;
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void project_split_kernel(
+    ProjectParams p) {
+  constexpr int NS = kSplitSlots;
+  constexpr int SLOT = (2 + 4) * 512;  // u16 per ring slot: 2 X fragments, then 4 W fragments
+  static_assert(4 * NS * SLOT * 2 >= 64 * (128 + 8) * 2, "the low-rank blocks stage rows in the same LDS");
+  extern __shared__ __attribute__((aligned(16))) u16 s_pr[];
+  const int b = blockIdx.x;
+  if (b >= 8 * p.per_xcd) {
+    append_block(p.app, b - 8 * p.per_xcd, reinterpret_cast<char*>(s_pr));
+    return;
+  }
+  // Block b runs on XCD b % 8: each XCD takes a contiguous run of tiles.
+  const int lb = (b % 8) * p.per_xcd + b / 8;
+  if (lb >= p.n_gemm) return;
+  const int ug = lb;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n = lane & 15, qd = lane >> 4;
+  const int unit = ug / 2;
+  const int half = ug % 2;  // feature tiles half and half + 2 of the unit
+  const bool active = unit < p.n_units;
+  constexpr int UPH = D / 64;  // units per head
+  const int uc = active ? unit : p.n_units - 1;
+  const int head = uc / UPH, hu = uc % UPH;
+  const int H = p.hidden, nk = H / 64;
+  const int kbeg = wave * nk / 4;  // this wave's stages [kbeg, kbeg + kcnt)
+  const int kcnt = (wave + 1) * nk / 4 - kbeg;
+  u16* const ring = s_pr + wave * NS * SLOT;
+  // W is packed (pack_qkv_kernel): the unit's eight fragments of a stage are
+  // 8 KB of contiguous memory, so each copy is 1 KB contiguous and a wave
+  // streams its unit's weights front to back.
+  const __amdgpu_buffer_rsrc_t wr = byte_rsrc(p.w + (uint64_t)uc * nk * 8 * 512, nk * 8 * 1024);
+  // X fragment ks: lane (n, qd) copies token n, columns 32 ks + 8 qd + [0, 8).
+  // Rows past the job read as zero (buffer bounds).
+  const __amdgpu_buffer_rsrc_t xr = byte_rsrc(p.x + (uint64_t)p.row0 * H, p.rows * H * 2);
+  const int xoff0 = (n * H + 8 * qd) * 2;
+
+  // tile jj of the wave is feature tile half + 2 jj
+  f32x4 acc[1][2];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) acc[0][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Copies of stage s into ring slot s % NS: the two X fragments, then the
+  // wave's four W fragments. Stages past the end copy the last one again, so
+  // every stage issues the same copies and the wait below holds.
+  auto issue = [&](int s) {
+    if (kcnt == 0) return;
+    const int sc = kbeg + (s < kcnt ? s : kcnt - 1);
+    u16* slot = ring + (s % NS) * SLOT;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (void __attribute__((address_space(3)))*)(slot + ks * 512), 16,
+                                               xoff0 + (64 * sc + 32 * ks) * 2, 0, 0, 0);
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int j = half + 2 * jj;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (void __attribute__((address_space(3)))*)(slot + (2 + 2 * jj + ks) * 512),
+                                                 16, ((sc * 8 + 2 * j + ks) * 64 + lane) * 16, 0, 0, 0);
+      }
+  };
+  // Before stage s: stages s .. s + NS - 2 are in flight (six copies each);
+  // with no more than NS - 2 stages' worth outstanding, stage s has landed.
+  // Every wave reads only its own ring.
+  constexpr int kAfter = (NS - 2) * 6;
+  constexpr int kWaitStage = (kAfter & 15) | ((kAfter >> 4) << 14) | (7 << 4) | (15 << 8);
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue(s);
+  for (int s = 0; s < kcnt; ++s) {
+    __builtin_amdgcn_s_waitcnt(kWaitStage);
+    issue(s + NS - 1);
+    const u16* slot = ring + (s % NS) * SLOT;
+    bf16x8 bx[2], aw[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        aw[ks][jj] = *reinterpret_cast<const bf16x8*>(slot + (2 + 2 * jj + ks) * 512 + lane * 8);
+      bx[ks] = *reinterpret_cast<const bf16x8*>(slot + ks * 512 + lane * 8);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        acc[0][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[ks][jj], bx[ks], acc[0][jj], 0, 0, 0);
+    // every LDS read of the stage first, then the MFMAs (the first ones wait
+    // only for their own operands)
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  }
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): no copy outlives the wave
+  // waves 1..3 hand their partial sums to wave 0 (added in wave order)
+  __syncthreads();  // every wave is done with its ring
+  float* red = reinterpret_cast<float*>(s_pr);  // [3][64 lanes][8]
+  if (wave > 0) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) *reinterpret_cast<f32x4*>(red + ((wave - 1) * 64 + lane) * 8 + 4 * jj) = acc[0][jj];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) acc[0][jj] += *reinterpret_cast<const f32x4*>(red + (w * 64 + lane) * 8 + 4 * jj);
+  if (!active) return;
+  project_epilogue<D, 1, 2>(p, acc, 0, head, hu, half);
+}
+
+// Calls of hundreds of rows and more: a workgroup takes 128 tokens and NH
+// half units (32 output features each: feature tiles h and h + 2 of a unit,
+// the two members of its rotary pairs) and streams both operands through LDS
+// (per 64-column stage, X 16 KB and W 4 NH KB; X token-major, each copy
+// reading whole cache lines). NH = 4 (two units) gives each byte copied twice
+// the flops of the four-unit, 32-row tile; NH = 3 makes 4/3 as many tiles,
+// for calls whose two-unit tiles would leave CUs idle. Compute wave w takes
+// tokens 64 (w / NH) .. + 63 and half unit w % NH, two waves per SIMD, so one
+// wave's LDS reads run under the other's MFMAs. Four copy waves, one per SIMD,
+// issue the stage's buffer-to-LDS copies: a wave that issues copies waits
+// while the CU's address and data units take them, and none of that wait
+// falls on the compute waves. A ring of NS slots keeps the copies NS - 2
+// stages ahead of the stage whose operands are read. Blocks after the GEMM
+// blocks compute the low-rank rows with the append code (four waves; the
+// others end at once, and a barrier waits only for waves that have not ended).
+constexpr int kWideRows = 128;  // tokens per tile of the wide form
+
+// s_waitcnt WAIT, then a bare s_barrier; no LDS access moves across either.
+template <int WAIT>
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(WAIT);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+template <int D, int NS, int NH>
+__global__ __launch_bounds__(64 * (2 * NH + 4)) void project_wide_kernel(ProjectParams p) {
+  static_assert(NH == 3 || NH == 4, "three or four half units per tile");
+  constexpr int CW = 2 * NH;               // compute waves
+  constexpr int SLOT = (16 + 4 * NH) * 512;  // u16 per ring slot: 16 X copies, then 4 W fragments per half unit
+  constexpr int NCP = 4 + NH;              // copies per copy wave and stage
+  static_assert(NS * SLOT * 2 >= 64 * (128 + 8) * 2, "the low-rank blocks stage rows in the same LDS");
+  static_assert(NS >= 4, "stage s + 1 is read while stage s + NS - 1 is copied into the slot of stage s - 1");
+  extern __shared__ __attribute__((aligned(16))) u16 s_pw[];
+  const int b = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (b >= 8 * p.per_xcd) {
+    if (wave >= 4) return;  // a wave-uniform exit
+    append_block(p.app, b - 8 * p.per_xcd, reinterpret_cast<char*>(s_pw));
+    return;
+  }
+  // block b runs on XCD b % 8; token tile fastest, so the token tiles of one
+  // column of half units read W through one L2
+  const int lb = (b % 8) * p.per_xcd + b / 8;
+  if (lb >= p.n_gemm) return;
+  const int ct = lb / p.tok_tiles, tt = lb % p.tok_tiles;
+  const int H = p.hidden, nk = H / 64;
+  // Before the MFMAs of stage s, the copy waves wait until their copies of
+  // stage s + 1 have landed (later stages may remain in flight) and the
+  // compute waves until every LDS read they issued has returned. The barrier
+  // then publishes stage s + 1 and retires the reads of the slot the next
+  // copies overwrite. It is a bare barrier: a workgroup fence would wait for
+  // every copy in flight.
+  if (wave >= CW) {
+    const int cw = wave - CW;
+    // X copy xi (tokens 8 xi .. 8 xi + 7 of the tile): lane l writes LDS
+    // bytes 16 l of the copy, token 8 xi + l / 8, the 16-byte chunk
+    // (l % 8) ^ (token % 8) of the token's 64 columns. Each eight lanes read
+    // one token's 128 contiguous bytes (a single cache line), and the XOR
+    // swizzle keeps the compute waves' operand reads free of bank conflicts.
+    // Rows past the job read as zero (buffer bounds).
+    const __amdgpu_buffer_rsrc_t xr = byte_rsrc(p.x + (uint64_t)p.row0 * H, p.rows * H * 2);
+    const int xt = lane >> 3, xc = (lane & 7) ^ (xt & 7);  // token in the copy, chunk it reads
+    const int xoff0 = ((tt * kWideRows + xt) * H + 8 * xc) * 2;
+    // W copy wi = 4 hs + 2 jj + ks: k-step ks of feature tile half + 2 jj of
+    // the tile's half unit hs (packed: 1 KB contiguous per copy); a half unit
+    // past the last reads the last unit
+    const __amdgpu_buffer_rsrc_t wr = byte_rsrc(p.w, p.n_units * nk * 8 * 1024);
+    // Stages past the end copy the last one again, so every stage issues the
+    // same copies and the wait counts hold.
+    auto issue = [&](int s) {
+      const int sc = s < nk ? s : nk - 1;
+      u16* slot = s_pw + (s % NS) * SLOT;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int xi = cw + 4 * i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (void __attribute__((address_space(3)))*)(slot + xi * 512), 16,
+                                                 xoff0 + (8 * xi * H + 64 * sc) * 2, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < NH; ++i) {
+        const int wi = cw + 4 * i, gh = NH * ct + (wi >> 2);
+        const int u = min(gh >> 1, p.n_units - 1);
+        const int f = 2 * ((gh & 1) + 2 * ((wi >> 1) & 1)) + (wi & 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (void __attribute__((address_space(3)))*)(slot + (16 + wi) * 512),
+                                                 16, ((u * nk + sc) * 8 + f) * 1024 + lane * 16, 0, 0, 0);
+      }
+    };
+    constexpr int kFirst = (NS - 2) * NCP, kAfter = (NS - 3) * NCP;
+    constexpr int kWaitFirst = (kFirst & 15) | ((kFirst >> 4) << 14) | (7 << 4) | (15 << 8);
+    constexpr int kWaitCopies = (kAfter & 15) | ((kAfter >> 4) << 14) | (7 << 4) | (15 << 8);
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) issue(s);
+    stage_barrier<kWaitFirst>();  // stage 0 has landed
+    for (int s = 0; s < nk; ++s) {
+      stage_barrier<kWaitCopies>();  // stage s + 1 has landed
+      issue(s + NS - 1);  // into the slot of stage s - 1, whose reads ended before the last barrier
+    }
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): no copy outlives the wave
+    return;
+  }
+  const int rh = wave / NH, hs = wave % NH;
+  const int gh = NH * ct + hs;
+  const int unit = gh >> 1, half = gh & 1;
+  f32x4 acc[4][2];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) acc[c][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // B operand (token 16 c' + n, columns 32 ks + 8 qd of the stage, c' the
+  // wave's token tile 4 rh + c): the swizzled 16-byte chunk 4 ks + qd
+  const int n = lane & 15, qd = lane >> 4;
+  int xrd[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) xrd[ks] = (64 * rh + n) * 64 + (((4 * ks + qd) ^ (n & 7)) << 3);
+  // Operands of one stage in registers, two sets: the reads of stage s + 1
+  // are in flight while stage s's MFMAs issue.
+  struct Ops {
+    bf16x8 bx[2][4], aw[2][2];
+  };
+  auto read = [&](int s, Ops& o) {
+    const u16* slot = s_pw + (s % NS) * SLOT;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        o.aw[ks][jj] = *reinterpret_cast<const bf16x8*>(slot + (16 + 4 * hs + 2 * jj + ks) * 512 + lane * 8);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o.bx[ks][c] = *reinterpret_cast<const bf16x8*>(slot + xrd[ks] + c * 16 * 64);
+    }
+  };
+  auto mma = [&](const Ops& o) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc[c][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.aw[ks][jj], o.bx[ks][c], acc[c][jj], 0, 0, 0);
+  };
+  constexpr int kWaitReads = 15 | (7 << 4) | (3 << 14);  // lgkmcnt(0)
+  Ops oa, ob;
+  stage_barrier<kWaitReads>();
+  read(0, oa);
+  // Stage nk (read in the last round) is a copy of stage nk - 1 that is
+  // never used.
+  for (int s = 0; s < nk; s += 2) {
+    stage_barrier<kWaitReads>();
+    read(s + 1, ob);
+    mma(oa);
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // the reads first, then the MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    if (s + 1 == nk) break;
+    stage_barrier<kWaitReads>();
+    read(s + 2, oa);
+    mma(ob);
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+  }
+  if (unit >= p.n_units) return;
+  constexpr int UPH = D / 64;  // units per head
+  project_epilogue<D, 4, 2>(p, acc, tt * kWideRows + 64 * rh, unit / UPH, unit % UPH, half);
 }
 
 // Packs W [(Hq + 2 Hkv) D][hidden] for project_kernel: for 64-feature unit u
@@ -2253,28 +2383,43 @@ int dev_append(const Geometry& g, const AppendJob& job) {
   return launch(g, job.do_kv ? 0 : 1, append_kernel, dim3(std::max(blocks, 1)), 0, p, "append_kernel");
 }
 
-// The GEMM part takes one 16-token tile in the split form for a few rows (a
-// decode step) and 32- or 64-token tiles otherwise (measured: the split form
-// over several row tiles is slower than 64-row tiles already at 64 rows).
+// The GEMM part takes the split form up to 16 rows (a decode step) and the
+// wide form beyond (measured 1.2-1.9x faster than 32- and 64-row tiles of four
+// units from 24 to 2,048 rows at the llama3 and qwen3 shapes, equal at 4,096).
 constexpr int kProjectSplitRows = 16;
-template <int D, int TM, bool SK>
-int launch_project_t(const Geometry& g, const ProjectParams& p) {
-  const size_t lds = (size_t)(SK ? 4 : 1) * project_slots(SK) * (2 * TM / 16 + (SK ? 4 : 32)) * 512 * sizeof(u16);
-  // the ring exceeds the default dynamic LDS limit (set once per process)
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(project_kernel<D, TM, SK>),
+template <int D>
+int launch_project_split(const Geometry& g, const ProjectParams& p) {
+  const size_t lds = (size_t)4 * kSplitSlots * 6 * 512 * sizeof(u16);
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(project_split_kernel<D>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) {
-    set_err("hipFuncSetAttribute(project_kernel)", attr);
+    set_err("hipFuncSetAttribute(project_split_kernel)", attr);
     return SKV_ERR_HIP;
   }
   const int grid = 8 * p.per_xcd + append_blocks(p.app);
-  return launch(g, 5, project_kernel<D, TM, SK>, dim3(grid), lds, p, "project_kernel");
+  return launch(g, 5, project_split_kernel<D>, dim3(grid), lds, p, "project_split_kernel");
+}
+
+constexpr int kWideSlots = 4;  // ring slots of the wide form
+template <int D, int NH>
+int launch_project_wide(const Geometry& g, const ProjectParams& p) {
+  const size_t lds = (size_t)kWideSlots * (16 + 4 * NH) * 512 * sizeof(u16);
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(project_wide_kernel<D, kWideSlots, NH>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) {
+    set_err("hipFuncSetAttribute(project_wide_kernel)", attr);
+    return SKV_ERR_HIP;
+  }
+  const int grid = 8 * p.per_xcd + append_blocks(p.app);
+  return launch(g, 5, project_wide_kernel<D, kWideSlots, NH>, dim3(grid), lds, p, "project_wide_kernel",
+                64 * (2 * NH + 4));
 }
 
 template <int D>
-int launch_project(const Geometry& g, const ProjectParams& p, int tm) {
-  if (tm == 16) return launch_project_t<D, 16, true>(g, p);
-  return tm == 32 ? launch_project_t<D, 32, false>(g, p) : launch_project_t<D, 64, false>(g, p);
+int launch_project(const Geometry& g, const ProjectParams& p, bool split, int nh) {
+  if (split) return launch_project_split<D>(g, p);
+  return nh == 3 ? launch_project_wide<D, 3>(g, p) : launch_project_wide<D, 4>(g, p);
 }
 
 int dev_pack_qkv(const Geometry& g, const uint16_t* w, uint16_t* out) {
@@ -2302,13 +2447,28 @@ int dev_project(const Geometry& g, const ProjectJob& job) {
   p.row0 = a.spans[0].src_row;
   p.rows = a.spans[a.n_spans - 1].src_row + a.spans[a.n_spans - 1].n - p.row0;
   p.n_units = (g.Hq + 2 * g.Hkv) * g.D / 64;
-  // up to 16 rows: half a unit per workgroup (split K); more rows: four
-  // units and 64 rows per workgroup, or 32 while 64-row tiles would not give
-  // every CU a workgroup (measured 1.25x faster at 64-512 rows, slower beyond)
-  const int groups = (p.n_units + 3) / 4;
-  const int tm = p.rows <= kProjectSplitRows ? 16 : (groups * ((p.rows + 63) / 64) < kCUs ? 32 : 64);
-  p.tok_tiles = (p.rows + tm - 1) / tm;
-  p.n_gemm = (tm == 16 ? 2 * p.n_units : (p.n_units + 3) / 4) * p.tok_tiles;
+  // up to 16 rows: half a unit per workgroup (split K); more rows: tiles of
+  // 128 tokens and three or four half units, whichever moves fewer bytes per
+  // CU (rounds of workgroups over the CUs, the low-rank blocks included, x
+  // bytes per tile: 16 + 4 NH KB a stage)
+  const int nk = g.hidden / 64;
+  const bool split = p.rows <= kProjectSplitRows;
+  if (!split && (int64_t)p.n_units * nk * 8 * 1024 >= ((int64_t)1 << 31)) {
+    set_err("project: packed weights of 2 GiB or more", hipErrorInvalidValue);
+    return SKV_ERR_UNSUPPORTED;
+  }
+  int nh = 4;
+  if (split) {
+    p.tok_tiles = 1;
+    p.n_gemm = 2 * p.n_units;
+  } else {
+    p.tok_tiles = (p.rows + kWideRows - 1) / kWideRows;
+    const int64_t app = append_blocks(p.app);
+    const int64_t t4 = (int64_t)(2 * p.n_units + 3) / 4 * p.tok_tiles + app;
+    const int64_t t3 = (int64_t)(2 * p.n_units + 2) / 3 * p.tok_tiles + app;
+    if ((t3 + kCUs - 1) / kCUs * 7 < (t4 + kCUs - 1) / kCUs * 8) nh = 3;
+    p.n_gemm = (2 * p.n_units + nh - 1) / nh * p.tok_tiles;
+  }
   p.per_xcd = (p.n_gemm + 7) / 8;
   p.Hq = g.Hq;
   p.Hkv = g.Hkv;
@@ -2316,7 +2476,7 @@ int dev_project(const Geometry& g, const ProjectJob& job) {
   p.rope = job.theta != 0.f;
   for (int s = 0; s < a.n_spans; ++s) p.view_off[s] = job.view_off[s];
   for (int i = 0; i < g.D / 2; ++i) p.inv_freq[i] = p.rope ? std::pow((double)job.theta, -2.0 * i / g.D) : 0.0;
-  return g.D == 128 ? launch_project<128>(g, p, tm) : launch_project<64>(g, p, tm);
+  return g.D == 128 ? launch_project<128>(g, p, split, nh) : launch_project<64>(g, p, split, nh);
 }
 
 // Decode for the agents of job, in groups that fit one launch. With app (a

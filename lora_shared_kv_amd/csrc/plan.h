@@ -114,4 +114,16 @@ inline int plan_check_prefill(const AttnJob& job, char* msg, size_t cap) {
   return SKV_OK;
 }
 
+// SKV_OK if the front end can stream the packed projection weights: the wide
+// form addresses them with 32-bit byte offsets, so they must stay below 2 GiB.
+inline int plan_check_project(const Geometry& g, char* msg, size_t cap) {
+  const uint64_t bytes = (uint64_t)(g.Hq + 2 * g.Hkv) * g.D * g.hidden * 2;
+  if (bytes >= (1ull << 31)) {
+    snprintf(msg, cap, "packed projection weights of %llu bytes (the front end takes less than 2 GiB)",
+             (unsigned long long)bytes);
+    return SKV_ERR_UNSUPPORTED;
+  }
+  return SKV_OK;
+}
+
 }  // namespace skv

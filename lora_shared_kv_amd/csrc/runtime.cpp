@@ -739,6 +739,11 @@ int skv_project_append(skv_ctx* c, int layer, int n, const int* agents, const in
   long total = 0;
   int rc = check_agent_rows(c, layer, n, agents, counts, &total, arg_err);
   if (rc != SKV_OK || total == 0) return rc;
+  {
+    char msg[160];
+    rc = skv::plan_check_project(c->g, msg, sizeof msg);
+    if (rc != SKV_OK) return c->fail(rc, "%s", msg);
+  }
   AgentRows ar;
   rc = plan_agent_rows(c, layer, n, agents, counts, nullptr, nullptr, A ? x : nullptr, A, ar);
   if (rc != SKV_OK) return rc;

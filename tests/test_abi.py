@@ -88,8 +88,10 @@ def test_bench_kernel_names_follow_the_library_choices():
     kernels = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                                 "lora_shared_kv_amd", "csrc", "kernels.hip")).read()
     assert bench.split_kernel_name(128, 16, 1, 8) == "decode_split_kernel<128,1,1>"
-    assert bench.project_kernel_name(32, 8, 128, 4) == "project_kernel<128,16,true>"
-    assert bench.project_kernel_name(32, 8, 128, 512) == "project_kernel<128,32,false>"
-    assert bench.project_kernel_name(32, 8, 128, 2048) == "project_kernel<128,64,false>"
-    for tm, sk in ((16, "true"), (32, "false"), (64, "false")):
-        assert f"launch_project_t<D, {tm}, {sk}>" in kernels
+    assert bench.project_kernel_name(32, 8, 128, 4) == "project_split_kernel<128>"
+    assert bench.project_kernel_name(32, 8, 128, 384) == "project_wide_kernel<128,4,3>"
+    assert bench.project_kernel_name(32, 8, 128, 512) == "project_wide_kernel<128,4,4>"
+    assert bench.project_kernel_name(32, 8, 128, 2048) == "project_wide_kernel<128,4,4>"
+    assert "launch_project_split<D>(g, p)" in kernels
+    for nh in (3, 4):
+        assert f"launch_project_wide<D, {nh}>(g, p)" in kernels

@@ -137,6 +137,8 @@ QWEN3_HEADS = Shape("qwen3-1.7b-heads", 1, 16, 8, 128, 2048, 16, 2, BASE_SHARED,
 TINY_HEADS = Shape("tiny-d64", 1, 14, 2, 64, 896, 8, 2, BASE_SHARED, 0)
 SMALL = Shape("small-d128", 1, 8, 2, 128, 512, 16, 2, BASE_SHARED, 0)
 MANY = Shape("many-agent-heads", 1, 16, 8, 128, 2048, 16, 8, BASE_SHARED, 0)
+# head dim 64 with five 64-feature units: the last column of two-unit tiles holds one unit
+ODD_UNITS = Shape("odd-units-d64", 1, 3, 1, 64, 256, 8, 2, BASE_SHARED, 0)
 
 
 @pytest.mark.parametrize("name,shape,prefix,own,counts,theta", [
@@ -216,3 +218,21 @@ def test_project_append_many_agents_suffix_rows():
     # 4 x 512 rows: 64-row tiles over the whole chip, agent boundaries on tile edges
     run_case(MANY, 4096, [0] * 8, [512, 0, 512, 0, 512, 0, 512, 0], 1000000.0, seed=15, attend=False)
 
+
+
+def test_project_append_wide_tiles():
+    # 555 rows over three agents (the wide form: 128-token tiles of two units):
+    # agent boundaries inside tiles, a partly filled last tile, and a 5-row
+    # agent whose low-rank rows take the dot-product blocks
+    run_case(LLAMA3_HEADS, 200, [0, 7, 0, 64], [300, 5, 0, 250], 500000.0, seed=16)
+
+
+def test_project_append_wide_tiles_odd_units():
+    # 301 rows, head dim 64, five units: the last tile column has idle waves
+    run_case(ODD_UNITS, 96, [0, 3], [260, 41], 10000.0, seed=17)
+
+
+def test_project_append_wide_tiles_three_half_units():
+    # 384 rows of the llama3 shapes: tiles of three half units (64 of them per
+    # 128 tokens, so that every CU takes one), an agent boundary inside a tile
+    run_case(LLAMA3_HEADS, 64, [0, 0, 9, 0], [200, 0, 184, 0], 500000.0, seed=18)
