@@ -108,16 +108,20 @@ def project_bytes(Hq, Hkv, d, hidden, r, rows, planes):
 def project_kernel_name(Hq, Hkv, d, rows):
     """Template arguments the library picks for a front-end call of one
     agent's rows: the split form up to 16 rows, else 128-token tiles of three
-    or four half units, whichever gives fewer rounds of workgroups over the
-    256 CUs (the low-rank blocks included) times bytes per tile."""
+    or four half units or 256-token tiles of four, whichever gives the fewest
+    rounds of workgroups over the 256 CUs (the low-rank blocks included) times
+    bytes copied per tile and stage (28, 32 and 48 KB)."""
     if rows <= 16:
         return f"project_split_kernel<{d}>"
     units = (Hq + 2 * Hkv) * d // 64
-    tiles = -(-rows // 128)
     app = -(-rows // 16) if rows > 8 else rows
-    t4 = -(-2 * units // 4) * tiles + app
-    t3 = -(-2 * units // 3) * tiles + app
-    nh = 3 if -(-t3 // 256) * 7 < -(-t4 // 256) * 8 else 4
+    t128, t256 = -(-rows // 128), -(-rows // 256)
+    c4 = -(-(-(-2 * units // 4) * t128 + app) // 256) * 32
+    c3 = -(-(-(-2 * units // 3) * t128 + app) // 256) * 28
+    ct = -(-(-(-2 * units // 4) * t256 + app) // 256) * 48
+    if ct < c4 and ct < c3:
+        return f"project_tall_kernel<{d}>"
+    nh = 3 if c3 < c4 and c3 <= ct else 4
     return f"project_wide_kernel<{d},4,{nh}>"
 
 

@@ -2128,6 +2128,113 @@ __global__ __launch_bounds__(64 * (2 * NH + 4)) void project_wide_kernel(Project
   project_epilogue<D, 4, 2>(p, acc, tt * kWideRows + 64 * rh, unit / UPH, unit % UPH, half);
 }
 
+// Calls of a thousand rows and more: 256 tokens x two units (128 features)
+// per workgroup, so each byte copied serves 4/3 the flops of the 128-token
+// tile (X 32 KB and W 16 KB per 64-column stage for 4 MFLOP). Compute wave w
+// takes tokens 64 (w / 2) .. + 63 and the whole unit w % 2 (feature tiles 0-3;
+// tiles j and j + 2 are rotary pairs); with 64 accumulator registers it reads
+// one stage at a time, the k-step 1 operands under the k-step 0 MFMAs. Four
+// copy waves keep the copies of a three-slot ring two stages ahead.
+constexpr int kTallRows = 256;  // tokens per tile of the tall form
+template <int D>
+__global__ __launch_bounds__(64 * 12) void project_tall_kernel(ProjectParams p) {
+  constexpr int NS = 3;
+  constexpr int SLOT = 48 * 512;  // u16 per ring slot: 32 X copies, then 8 W fragments of each unit
+  constexpr int NCP = 12;         // copies per copy wave and stage
+  extern __shared__ __attribute__((aligned(16))) u16 s_pt[];
+  const int b = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (b >= 8 * p.per_xcd) {
+    if (wave >= 4) return;  // a wave-uniform exit
+    append_block(p.app, b - 8 * p.per_xcd, reinterpret_cast<char*>(s_pt));
+    return;
+  }
+  const int lb = (b % 8) * p.per_xcd + b / 8;
+  if (lb >= p.n_gemm) return;
+  const int ct = lb / p.tok_tiles, tt = lb % p.tok_tiles;
+  const int H = p.hidden, nk = H / 64;
+  if (wave >= 8) {
+    const int cw = wave - 8;
+    // X copy xi (tokens 8 xi .. 8 xi + 7 of the tile) as in the wide form:
+    // token-major, XOR-swizzled 16-byte chunks, whole cache lines per copy
+    const __amdgpu_buffer_rsrc_t xr = byte_rsrc(p.x + (uint64_t)p.row0 * H, p.rows * H * 2);
+    const int xt = lane >> 3, xc = (lane & 7) ^ (xt & 7);
+    const int xoff0 = ((tt * kTallRows + xt) * H + 8 * xc) * 2;
+    const __amdgpu_buffer_rsrc_t wr = byte_rsrc(p.w, p.n_units * nk * 8 * 1024);
+    auto issue = [&](int s) {
+      const int sc = s < nk ? s : nk - 1;
+      u16* slot = s_pt + (s % NS) * SLOT;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int xi = cw + 4 * i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (void __attribute__((address_space(3)))*)(slot + xi * 512), 16,
+                                                 xoff0 + (8 * xi * H + 64 * sc) * 2, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int fi = cw + 4 * i;  // fragment fi % 8 of unit fi / 8 of the tile
+        const int u = min(2 * ct + (fi >> 3), p.n_units - 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (void __attribute__((address_space(3)))*)(slot + (32 + fi) * 512),
+                                                 16, ((u * nk + sc) * 8 + (fi & 7)) * 1024 + lane * 16, 0, 0, 0);
+      }
+    };
+    // before stage s: its copies have landed (stage s + 1 may be in flight)
+    constexpr int kAfter = (NS - 2) * NCP;
+    constexpr int kWaitCopies = (kAfter & 15) | ((kAfter >> 4) << 14) | (7 << 4) | (15 << 8);
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) issue(s);
+    for (int s = 0; s < nk; ++s) {
+      stage_barrier<kWaitCopies>();
+      issue(s + NS - 1);  // into the slot of stage s - 1, whose reads ended before this barrier
+    }
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): no copy outlives the wave
+    return;
+  }
+  const int rh = wave >> 1, u2 = wave & 1;
+  const int unit = 2 * ct + u2;
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[c][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int n = lane & 15, qd = lane >> 4;
+  int xrd[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) xrd[ks] = (64 * rh + n) * 64 + (((4 * ks + qd) ^ (n & 7)) << 3);
+  constexpr int kWaitReads = 15 | (7 << 4) | (3 << 14);  // lgkmcnt(0)
+  for (int s = 0; s < nk; ++s) {
+    stage_barrier<kWaitReads>();
+    const u16* slot = s_pt + (s % NS) * SLOT;
+    bf16x8 bx[2][4], aw[2][4];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        aw[ks][j] = *reinterpret_cast<const bf16x8*>(slot + (32 + 8 * u2 + 2 * j + ks) * 512 + lane * 8);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bx[ks][c] = *reinterpret_cast<const bf16x8*>(slot + xrd[ks] + c * 16 * 64);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc[c][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[ks][j], bx[ks][c], acc[c][j], 0, 0, 0);
+    // k-step 0's reads, then its MFMAs with k-step 1's reads among them, then k-step 1's MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+  }
+  if (unit >= p.n_units) return;
+  constexpr int UPH = D / 64;  // units per head
+  project_epilogue<D, 4, 4>(p, acc, tt * kTallRows + 64 * rh, unit / UPH, unit % UPH, 0);
+}
+
 // Packs W [(Hq + 2 Hkv) D][hidden] for project_kernel: for 64-feature unit u
 // (head u / (D / 64), d in [32 hu, 32 hu + 32) and that + D/2), 64-column
 // stage s, fragment f = 2 j + ks and lane l = n + 16 qd, the 16 bytes at
@@ -2384,8 +2491,9 @@ int dev_append(const Geometry& g, const AppendJob& job) {
 }
 
 // The GEMM part takes the split form up to 16 rows (a decode step) and the
-// wide form beyond (measured 1.2-1.9x faster than 32- and 64-row tiles of four
-// units from 24 to 2,048 rows at the llama3 and qwen3 shapes, equal at 4,096).
+// wide or tall form beyond (the wide form measured 1.2-1.9x faster than 32-
+// and 64-row tiles of four units from 24 to 2,048 rows at the llama3 and qwen3
+// shapes; the tall form 1.08-1.3x faster than the wide one where it is taken).
 constexpr int kProjectSplitRows = 16;
 template <int D>
 int launch_project_split(const Geometry& g, const ProjectParams& p) {
@@ -2417,8 +2525,23 @@ int launch_project_wide(const Geometry& g, const ProjectParams& p) {
 }
 
 template <int D>
+int launch_project_tall(const Geometry& g, const ProjectParams& p) {
+  const size_t lds = (size_t)3 * 48 * 512 * sizeof(u16);
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(project_tall_kernel<D>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) {
+    set_err("hipFuncSetAttribute(project_tall_kernel)", attr);
+    return SKV_ERR_HIP;
+  }
+  const int grid = 8 * p.per_xcd + append_blocks(p.app);
+  return launch(g, 5, project_tall_kernel<D>, dim3(grid), lds, p, "project_tall_kernel", 64 * 12);
+}
+
+// nh: 3 or 4 half units per 128-token tile, or 0 for the tall form
+template <int D>
 int launch_project(const Geometry& g, const ProjectParams& p, bool split, int nh) {
   if (split) return launch_project_split<D>(g, p);
+  if (nh == 0) return launch_project_tall<D>(g, p);
   return nh == 3 ? launch_project_wide<D, 3>(g, p) : launch_project_wide<D, 4>(g, p);
 }
 
@@ -2462,12 +2585,17 @@ int dev_project(const Geometry& g, const ProjectJob& job) {
     p.tok_tiles = 1;
     p.n_gemm = 2 * p.n_units;
   } else {
-    p.tok_tiles = (p.rows + kWideRows - 1) / kWideRows;
+    // rounds of workgroups over the CUs x KB copied per stage of a tile:
+    // 128 tokens x 3 half units 28, x 4 half units 32, 256 tokens x 4 48
     const int64_t app = append_blocks(p.app);
-    const int64_t t4 = (int64_t)(2 * p.n_units + 3) / 4 * p.tok_tiles + app;
-    const int64_t t3 = (int64_t)(2 * p.n_units + 2) / 3 * p.tok_tiles + app;
-    if ((t3 + kCUs - 1) / kCUs * 7 < (t4 + kCUs - 1) / kCUs * 8) nh = 3;
-    p.n_gemm = (2 * p.n_units + nh - 1) / nh * p.tok_tiles;
+    const int64_t tt128 = (p.rows + kWideRows - 1) / kWideRows, tt256 = (p.rows + kTallRows - 1) / kTallRows;
+    const int64_t c4 = ((2 * p.n_units + 3) / 4 * tt128 + app + kCUs - 1) / kCUs * 32;
+    const int64_t c3 = ((2 * p.n_units + 2) / 3 * tt128 + app + kCUs - 1) / kCUs * 28;
+    const int64_t ct = ((2 * p.n_units + 3) / 4 * tt256 + app + kCUs - 1) / kCUs * 48;
+    if (c3 < c4 && c3 <= ct) nh = 3;
+    if (ct < c4 && ct < c3) nh = 0;
+    p.tok_tiles = (int)(nh == 0 ? tt256 : tt128);
+    p.n_gemm = (nh == 0 ? (p.n_units + 1) / 2 : (2 * p.n_units + nh - 1) / nh) * p.tok_tiles;
   }
   p.per_xcd = (p.n_gemm + 7) / 8;
   p.Hq = g.Hq;

@@ -91,7 +91,9 @@ def test_bench_kernel_names_follow_the_library_choices():
     assert bench.project_kernel_name(32, 8, 128, 4) == "project_split_kernel<128>"
     assert bench.project_kernel_name(32, 8, 128, 384) == "project_wide_kernel<128,4,3>"
     assert bench.project_kernel_name(32, 8, 128, 512) == "project_wide_kernel<128,4,4>"
-    assert bench.project_kernel_name(32, 8, 128, 2048) == "project_wide_kernel<128,4,4>"
+    assert bench.project_kernel_name(32, 8, 128, 1024) == "project_tall_kernel<128>"
+    assert bench.project_kernel_name(32, 8, 128, 4096) == "project_tall_kernel<128>"
     assert "launch_project_split<D>(g, p)" in kernels
     for nh in (3, 4):
         assert f"launch_project_wide<D, {nh}>(g, p)" in kernels
+    assert "launch_project_tall<D>(g, p)" in kernels

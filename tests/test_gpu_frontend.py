@@ -139,6 +139,8 @@ SMALL = Shape("small-d128", 1, 8, 2, 128, 512, 16, 2, BASE_SHARED, 0)
 MANY = Shape("many-agent-heads", 1, 16, 8, 128, 2048, 16, 8, BASE_SHARED, 0)
 # head dim 64 with five 64-feature units: the last column of two-unit tiles holds one unit
 ODD_UNITS = Shape("odd-units-d64", 1, 3, 1, 64, 256, 8, 2, BASE_SHARED, 0)
+# head dim 64 with 96 units, so that a thousand rows take 256-token tiles
+WIDE_D64 = Shape("wide-d64", 1, 64, 16, 64, 256, 8, 2, BASE_SHARED, 0)
 
 
 @pytest.mark.parametrize("name,shape,prefix,own,counts,theta", [
@@ -236,3 +238,14 @@ def test_project_append_wide_tiles_three_half_units():
     # 384 rows of the llama3 shapes: tiles of three half units (64 of them per
     # 128 tokens, so that every CU takes one), an agent boundary inside a tile
     run_case(LLAMA3_HEADS, 64, [0, 0, 9, 0], [200, 0, 184, 0], 500000.0, seed=18)
+
+
+def test_project_append_tall_tiles():
+    # 1,024 rows of the llama3 shapes: 256-token tiles of two units, with an
+    # agent boundary inside a tile and a partly filled last tile
+    run_case(LLAMA3_HEADS, 64, [0, 0, 0, 0], [600, 0, 424, 0], 500000.0, seed=19, attend=False)
+
+
+def test_project_append_tall_tiles_d64():
+    # head dim 64: 1,000 rows over two agents in 256-token tiles
+    run_case(WIDE_D64, 128, [0, 5], [700, 300], 10000.0, seed=20, attend=False)
