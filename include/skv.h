@@ -175,7 +175,8 @@ int skv_pack_qkv(skv_ctx* ctx, const skv_bf16* w_qkv, skv_bf16* w_packed);
  *   q_out: device [sum counts][Hq][d], written (bf16, rotated).
  * q, k and v are rounded once to bf16 from fp32 accumulation. Each agent's
  * own low-rank rows must be level with its base rows before the call.
- * Errors: ARG, STATE, OOM (nothing is appended). */
+ * Errors: ARG, STATE, OOM, and UNSUPPORTED when the packed weights
+ * ((Hq + 2 Hkv) d hidden bf16 values) reach 2 GiB (nothing is appended). */
 int skv_project_append(skv_ctx* ctx, int layer, int n, const int* agents, const int* counts,
                        const skv_bf16* x, const skv_bf16* w_packed, const skv_bf16* A,
                        float rope_theta, skv_bf16* q_out);

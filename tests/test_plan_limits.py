@@ -9,7 +9,8 @@ applies the same plan checks as the GPU build. The limits (plan.h):
     to the largest b_i, then every own suffix, each padded to 32 keys) holds at
     most 32 * 512 * min(2048 / Hkv, 1024) keys;
   prefill: a view spans at most 4096 pages of 64 rows (shared and own pages
-    counted separately).
+    counted separately);
+  front end: the packed projection weights stay below 2 GiB.
 """
 import pytest
 
@@ -154,3 +155,25 @@ def test_static_scratch_limit():
 
 def state16(c):
     return (B.skv_get_lens(c, 0), B.skv_get_counters(c), [B.skv_get_pages(c, 0, s) for s in range(-1, 16)])
+
+
+def test_front_end_weight_limit():
+    """The front end addresses the packed projection weights with 32-bit byte
+    offsets: a geometry whose packed weights reach 2 GiB is refused before
+    anything is planned, and the same call one column block smaller runs."""
+    def ctx_for(hidden):
+        cfg = dict(n_layers=1, n_q_heads=64, n_kv_heads=64, head_dim=128, hidden=hidden, rank=8, n_agents=2,
+                   mode=1, page_size=64, max_pages=16)
+        n = B.skv_arena_bytes(cfg, "host")
+        return B.skv_create(cfg, (1 << 24, n), None, "host")
+    big = 43712  # (64 + 128) * 128 * 43712 * 2 bytes >= 2 GiB
+    assert (64 + 2 * 64) * 128 * big * 2 >= 1 << 31 > (64 + 2 * 64) * 128 * (big - 64) * 2
+    c = ctx_for(big)
+    before = state(c)
+    with pytest.raises(B.SkvError) as e:
+        B.skv_project_append(c, 0, [0], [32], FAKE, FAKE, FAKE, 0.0, FAKE)
+    assert e.value.code == "UNSUPPORTED" and "2 GiB" in str(e.value)
+    assert state(c) == before
+    c = ctx_for(big - 64)
+    B.skv_project_append(c, 0, [0], [32], FAKE, FAKE, FAKE, 0.0, FAKE)
+    assert B.skv_get_lens(c, 0)["S"][0] == 32
