@@ -141,6 +141,8 @@ MANY = Shape("many-agent-heads", 1, 16, 8, 128, 2048, 16, 8, BASE_SHARED, 0)
 ODD_UNITS = Shape("odd-units-d64", 1, 3, 1, 64, 256, 8, 2, BASE_SHARED, 0)
 # head dim 64 with 96 units, so that a thousand rows take 256-token tiles
 WIDE_D64 = Shape("wide-d64", 1, 64, 16, 64, 256, 8, 2, BASE_SHARED, 0)
+# the llama3 heads with hidden 960: an odd number (15) of 64-column stages
+ODD_STAGES = Shape("odd-stages", 1, 32, 8, 128, 960, 8, 4, BASE_LR_SHARED, 0)
 
 
 @pytest.mark.parametrize("name,shape,prefix,own,counts,theta", [
@@ -249,3 +251,11 @@ def test_project_append_tall_tiles():
 def test_project_append_tall_tiles_d64():
     # head dim 64: 1,000 rows over two agents in 256-token tiles
     run_case(WIDE_D64, 128, [0, 5], [700, 300], 10000.0, seed=20, attend=False)
+
+
+@pytest.mark.parametrize("counts", [[7, 0, 5, 0], [200, 0, 100, 0], [700, 0, 0, 324]],
+                         ids=["split", "wide-3-half-units", "tall"])
+def test_project_append_odd_stage_count(counts):
+    # 15 stages of 64 hidden columns: the split form's quarters differ in
+    # length, and the wide and tall forms end on an odd stage
+    run_case(ODD_STAGES, 64, [0, 0, 0, 0], counts, 500000.0, seed=21, attend=False)
