@@ -287,50 +287,55 @@ __device__ void append_lr_zero_block(const AppendParams& p, int s, int pi) {
 // decode step appends one row per agent). Each thread takes 8 consecutive
 // hidden columns at a time with 16-byte loads of x and of the matching A rows,
 // so all of a thread's loads are independent and in flight together.
-template <int R, int NTA>
+template <int R, int NTA, int RG = R>
 __device__ void append_lr_dot_rows(const AppendParams& p, int s, int row, char* smem) {
   const skv::Span& sp = p.spans[s];
   const int H = p.hidden;
   const u16* x = p.x + (uint64_t)(sp.src_row + row) * H;
-  constexpr int VR = R >= 8 ? R / 8 : 1;  // 16-byte vectors per A row (r = 4 reads 8 bytes)
-  float acc[R];
-#pragma unroll
-  for (int k = 0; k < R; ++k) acc[k] = 0.f;
-#pragma unroll 2
-  for (int u8 = threadIdx.x; u8 < H / 8; u8 += NTA) {
-    const u32x4 xv = *reinterpret_cast<const u32x4*>(x + u8 * 8);
-    const u16* arow = sp.a + (uint64_t)u8 * 8 * R;
-    u32x4 av[8][VR];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int v = 0; v < VR; ++v) {
-        if (R >= 8) {
-          av[j][v] = *reinterpret_cast<const u32x4*>(arow + j * R + 8 * v);
-        } else {
-          u32x2 t = *reinterpret_cast<const u32x2*>(arow + j * R);
-          av[j][v] = u32x4{t[0], t[1], 0u, 0u};
-        }
-      }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t xw = xv[j / 2];
-      const float xf = __uint_as_float((j & 1) ? (xw & 0xffff0000u) : (xw << 16));
-#pragma unroll
-      for (int k = 0; k < R; ++k) {
-        const uint32_t aw = av[j][k / 8][(k % 8) / 2];
-        acc[k] += xf * __uint_as_float((k & 1) ? (aw & 0xffff0000u) : (aw << 16));
-      }
-    }
-  }
+  constexpr int VG = RG >= 8 ? RG / 8 : 1;  // 16-byte vectors per A row and rank group (r = 4 reads 8 bytes)
   float* red = reinterpret_cast<float*>(smem);  // [waves][R]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // ranks in groups of RG, one pass over the columns each (every rank's sum
+  // keeps the same order)
 #pragma unroll
-  for (int k = 0; k < R; ++k) {
-    float v = acc[k];
+  for (int k0 = 0; k0 < R; k0 += RG) {
+    float acc[RG];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    if (lane == 0) red[w * R + k] = v;
+    for (int k = 0; k < RG; ++k) acc[k] = 0.f;
+#pragma unroll 2
+    for (int u8 = threadIdx.x; u8 < H / 8; u8 += NTA) {
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(x + u8 * 8);
+      const u16* arow = sp.a + (uint64_t)u8 * 8 * R + k0;
+      u32x4 av[8][VG];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int v = 0; v < VG; ++v) {
+          if (R >= 8) {
+            av[j][v] = *reinterpret_cast<const u32x4*>(arow + j * R + 8 * v);
+          } else {
+            u32x2 t = *reinterpret_cast<const u32x2*>(arow + j * R);
+            av[j][v] = u32x4{t[0], t[1], 0u, 0u};
+          }
+        }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t xw = xv[j / 2];
+        const float xf = __uint_as_float((j & 1) ? (xw & 0xffff0000u) : (xw << 16));
+#pragma unroll
+        for (int k = 0; k < RG; ++k) {
+          const uint32_t aw = av[j][k / 8][(k % 8) / 2];
+          acc[k] += xf * __uint_as_float((k & 1) ? (aw & 0xffff0000u) : (aw << 16));
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < RG; ++k) {
+      float v = acc[k];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+      if (lane == 0) red[w * R + k0 + k] = v;
+    }
   }
   __syncthreads();
   if (threadIdx.x < R) {
@@ -343,13 +348,14 @@ __device__ void append_lr_dot_rows(const AppendParams& p, int s, int row, char* 
   }
 }
 
-template <int NTA>
+// LEAN: rank 32 in two groups of 16 (for kernels with a tight register budget)
+template <int NTA, bool LEAN = false>
 __device__ void append_lr_dot_block(const AppendParams& p, int s, int row, char* smem) {
   switch (p.r) {
     case 4: append_lr_dot_rows<4, NTA>(p, s, row, smem); break;
     case 8: append_lr_dot_rows<8, NTA>(p, s, row, smem); break;
     case 16: append_lr_dot_rows<16, NTA>(p, s, row, smem); break;
-    default: append_lr_dot_rows<32, NTA>(p, s, row, smem); break;
+    default: append_lr_dot_rows<32, NTA, LEAN ? 16 : 32>(p, s, row, smem); break;
   }
 }
 
@@ -497,8 +503,11 @@ __device__ void append_lr_mfma_block(const AppendParams& p, int s, int tile, cha
 // whether the kernel carries the K/V tile copies and the MFMA low-rank tiles:
 // launches whose jobs never hold such blocks leave that code out, which keeps
 // them small (the host checks the jobs it gives them). NTA threads of the
-// block run it (the first NTA; the MFMA low-rank tiles take four waves).
-template <bool KV = true, bool MFMA_LR = true, int NTA = 256>
+// block run it (the first NTA; the MFMA low-rank tiles take four waves). HS:
+// 64-column sections per slab of the MFMA low-rank tiles at ranks up to 16
+// (2 for kernels with a tight register budget, whose dot-product rows then
+// take rank 32 in two passes).
+template <bool KV = true, bool MFMA_LR = true, int NTA = 256, int HS = 4>
 __device__ void append_block(const AppendParams& p, int b, char* smem) {
   static_assert(!MFMA_LR || NTA == 256, "the MFMA low-rank tiles are written for four waves");
   if (b == 0 && p.update_tables) {
@@ -525,14 +534,14 @@ __device__ void append_block(const AppendParams& p, int b, char* smem) {
   if (p.lr_kind[s] == 0)
     append_lr_zero_block<NTA>(p, s, sub);
   else if (p.lr_kind[s] == 1)
-    append_lr_dot_block<NTA>(p, s, sub, smem);
+    append_lr_dot_block<NTA, HS == 2>(p, s, sub, smem);
   else if constexpr (MFMA_LR) {
     if (p.r == 4)
-      append_lr_mfma_block<0, 4>(p, s, sub, smem);
+      append_lr_mfma_block<0, HS>(p, s, sub, smem);
     else if (p.r == 8)
-      append_lr_mfma_block<1, 4>(p, s, sub, smem);
+      append_lr_mfma_block<1, HS>(p, s, sub, smem);
     else if (p.r == 16)
-      append_lr_mfma_block<2, 4>(p, s, sub, smem);
+      append_lr_mfma_block<2, HS>(p, s, sub, smem);
     else
       append_lr_mfma_block<4, 2>(p, s, sub, smem);
   }
@@ -2002,7 +2011,7 @@ __global__ __launch_bounds__(64 * (2 * NH + 4)) void project_wide_kernel(Project
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (b >= 8 * p.per_xcd) {
     if (wave >= 4) return;  // a wave-uniform exit
-    append_block(p.app, b - 8 * p.per_xcd, reinterpret_cast<char*>(s_pw));
+    append_block<false, true, 256, 2>(p.app, b - 8 * p.per_xcd, reinterpret_cast<char*>(s_pw));
     return;
   }
   // block b runs on XCD b % 8; token tile fastest, so the token tiles of one
@@ -2146,7 +2155,7 @@ __global__ __launch_bounds__(64 * 12) void project_tall_kernel(ProjectParams p) 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (b >= 8 * p.per_xcd) {
     if (wave >= 4) return;  // a wave-uniform exit
-    append_block(p.app, b - 8 * p.per_xcd, reinterpret_cast<char*>(s_pt));
+    append_block<false, true, 256, 2>(p.app, b - 8 * p.per_xcd, reinterpret_cast<char*>(s_pt));
     return;
   }
   const int lb = (b % 8) * p.per_xcd + b / 8;
