@@ -412,6 +412,8 @@ def main():
                     help="time the fused front end (skv_project_append) on one layer of the workload: "
                          "one row per agent (a decode step) and 512 rows of one agent (a suffix) (the default)")
     ap.add_argument("--no-frontend", action="store_true", help="skip the front-end leg")
+    ap.add_argument("--no-launch-pattern", action="store_true",
+                    help="skip the launch-pattern probe (the decode step's launches without their arithmetic)")
     ap.add_argument("--ttft-sweep", action="store_true",
                     help="only time the first token of a new role, reusing the cache versus re-prefilling it, "
                          "at the qwen3 8K takeover shapes and the qwen2.5 1k-8k contexts; prints one JSON line")
@@ -703,6 +705,25 @@ def main():
     if not args.no_frontend:
         frontend = frontend_timing(B, dict(c, n_layers=1), randn, reps=20)
 
+    # ---- the decode step's launch pattern without its arithmetic: per layer a
+    # streaming read of the split pass's algorithmic bytes by one workgroup per
+    # CU, then a small launch of one workgroup per query row ordered after it.
+    # Its step time bounds what any two-launch-per-layer decode step can reach
+    # on this machine ----
+    launch_pattern = None
+    if not args.no_launch_pattern and not args.no_events:
+        # the split pass's algorithmic bytes at the timed repetitions' middle step
+        lb = (decode_split_bytes(Hkv, d, r, hidden, base0, [mid_S] * N, N, Hq, bls=mode == 1) + 15) // 16 * 16
+        buf = torch.empty(L * lb, dtype=torch.uint8, device=dev)
+        pat_ms, str_ms = B.skv_probe_launch_pattern(buf, lb, L, steps=20, tail_blocks=N * Hq)
+        del buf
+        ceiling = N / (pat_ms / 1e3)
+        launch_pattern = {"layer_bytes": lb, "layers": L, "tail_blocks": N * Hq,
+                          "ms_per_step": round(pat_ms, 4), "ms_per_step_stream_only": round(str_ms, 4),
+                          "stream_only_gbs": round(L * lb / (str_ms / 1e3) / 1e9, 1),
+                          "tokens_per_s_ceiling": round(ceiling, 1),
+                          "frac_of_ceiling": round(value / ceiling, 4)}
+
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -733,6 +754,8 @@ def main():
         res["frontend"] = frontend
     if mixed is not None:
         res["mixed"] = mixed
+    if launch_pattern is not None:
+        res["launch_pattern"] = launch_pattern
     if not args.no_cpu_baseline and default_run:
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
     print(json.dumps(res), flush=True)

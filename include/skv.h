@@ -340,9 +340,22 @@ const char* skv_last_error(const skv_ctx* ctx);
  * skv_probe_mfma_bf16: a dense v_mfma_f32_16x16x32_bf16 issue loop, two waves
  *   per SIMD on every CU with independent accumulators; *tflops = the
  *   achieved dense bf16 rate (10^12 flop/s, 2 flops per multiply-add).
+ * skv_probe_launch_pattern: the launch pattern of a decode step without its
+ *   arithmetic. src holds `layers` consecutive buffers of layer_bytes bytes
+ *   (a multiple of 16, at least 1 MiB; caller-owned, contents irrelevant).
+ *   One step is, for every layer, a streaming read of that layer's buffer by
+ *   one workgroup per CU (non-temporal 16-byte loads) followed by a small
+ *   launch of tail_blocks workgroups that reads what the streaming launch
+ *   left (ordered after it, as a merge is after its split pass). After one
+ *   untimed step, `steps` steps are timed between two events; *ms_pattern =
+ *   ms per step (best of three runs), *ms_stream = the same without the small
+ *   launches. layers in [1, 1024], steps in [1, 1000], tail_blocks in
+ *   [1, 65535].
  * Errors: ARG (NULL pointers, bad sizes), HIP, UNSUPPORTED (CPU-only build). */
 int skv_probe_stream_read(const void* src, uint64_t bytes, int reps, void* stream, double* gbs);
 int skv_probe_mfma_bf16(void* stream, double* tflops);
+int skv_probe_launch_pattern(const void* src, uint64_t layer_bytes, int layers, int steps, int tail_blocks,
+                             void* stream, double* ms_pattern, double* ms_stream);
 
 #ifdef __cplusplus
 }

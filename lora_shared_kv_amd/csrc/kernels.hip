@@ -50,6 +50,9 @@ namespace skv {
 // Written by the probe kernels only on an impossible value; external linkage,
 // so the compiler must keep the work that feeds it.
 __device__ unsigned int probe_sink[4];
+// One word per wave of the launch-pattern probe's streaming launch (at most
+// four waves in each of kPlanCUs workgroups), read by the small launch after it.
+__device__ unsigned int probe_part[4 * kPlanCUs];
 }  // namespace skv
 
 // Static device scratch of skv_decode_step_static (callers that cannot
@@ -2309,6 +2312,35 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters) {
   if (t[0] + t[1] + t[2] + t[3] == 1234.5f) skv::probe_sink[threadIdx.x & 3] = __float_as_uint(t[0]);
 }
 
+// The launch-pattern probe's pair: a one-workgroup-per-CU streaming read of a
+// layer-sized buffer that leaves one word per wave, then a small launch of
+// single-row workgroups that reads those words (so it is ordered after the
+// read, as a merge is after its split pass).
+__global__ __launch_bounds__(256) void probe_layer_kernel(const u32x4* __restrict__ src, size_t n) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  u32x4 acc = {0, 0, 0, 0};
+  for (; i + 7 * stride < n; i += 8 * stride) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u];
+  }
+  for (; i < n; i += stride) acc ^= __builtin_nontemporal_load(src + i);
+  uint32_t a = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) a ^= __shfl_xor(a, o);
+  if ((threadIdx.x & 63) == 0) skv::probe_part[(blockIdx.x * 4 + (threadIdx.x >> 6)) % (4 * kCUs)] = a;
+}
+
+__global__ __launch_bounds__(256) void probe_tail_kernel() {
+  uint32_t a = skv::probe_part[(blockIdx.x * 256 + threadIdx.x) % (4 * kCUs)];
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) a ^= __shfl_xor(a, o);
+  if (a == 0x9e3779b9u) skv::probe_sink[threadIdx.x & 3] = a;
+}
+
 // ---------------------------------------------------------------------------
 // Host side: launch helpers, planning, timing
 // ---------------------------------------------------------------------------
@@ -2820,6 +2852,53 @@ int dev_probe_mfma_bf16(void* stream, double* tflops) {
   }
   const double flops = (double)kBlocks * 4 * kIters * 8 * (16.0 * 16 * 32 * 2);
   *tflops = flops / (ms * 1e-3) / 1e12;
+  return SKV_OK;
+}
+
+// `steps` steps of `layers` layers: per layer one probe_layer_kernel over that
+// layer's bytes, then (with_tail) one probe_tail_kernel of tail_blocks
+// workgroups; one untimed step first; ms per step, the best of three runs.
+static double probe_pattern_ms(hipStream_t st, const char* src, uint64_t layer_bytes, int layers, int steps,
+                               int tail_blocks, bool with_tail) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return -1.0;
+  const size_t n = (size_t)(layer_bytes / 16);
+  double best = 1e30;
+  for (int run = 0; run < 3 && best > 0; ++run) {
+    for (int s = -1; s < steps; ++s) {
+      if (s == 0) (void)hipEventRecord(a, st);
+      for (int l = 0; l < layers; ++l) {
+        hipLaunchKernelGGL(probe_layer_kernel, dim3(kCUs), dim3(256), 0, st,
+                           (const u32x4*)(src + (uint64_t)l * layer_bytes), n);
+        if (with_tail) hipLaunchKernelGGL(probe_tail_kernel, dim3(tail_blocks), dim3(256), 0, st);
+      }
+    }
+    (void)hipEventRecord(b, st);
+    if (hipGetLastError() != hipSuccess || hipEventSynchronize(b) != hipSuccess) {
+      best = -1.0;
+      break;
+    }
+    float ms = 0.f;
+    (void)hipEventElapsedTime(&ms, a, b);
+    best = std::min(best, (double)ms / steps);
+  }
+  (void)hipEventDestroy(a);
+  (void)hipEventDestroy(b);
+  return best;
+}
+
+int dev_probe_launch_pattern(const void* src, uint64_t layer_bytes, int layers, int steps, int tail_blocks,
+                             void* stream, double* ms_pattern, double* ms_stream) {
+  const hipStream_t st = (hipStream_t)stream;
+  const double pat = probe_pattern_ms(st, (const char*)src, layer_bytes, layers, steps, tail_blocks, true);
+  const double str = pat > 0 ? probe_pattern_ms(st, (const char*)src, layer_bytes, layers, steps, tail_blocks, false)
+                             : -1.0;
+  if (pat <= 0 || str <= 0) {
+    set_err("probe_layer_kernel / probe_tail_kernel", hipGetLastError());
+    return SKV_ERR_HIP;
+  }
+  *ms_pattern = pat;
+  *ms_stream = str;
   return SKV_OK;
 }
 

@@ -899,4 +899,12 @@ int skv_probe_mfma_bf16(void* stream, double* tflops) {
   return skv::dev_probe_mfma_bf16(stream, tflops);
 }
 
+int skv_probe_launch_pattern(const void* src, uint64_t layer_bytes, int layers, int steps, int tail_blocks,
+                             void* stream, double* ms_pattern, double* ms_stream) {
+  if (!src || !ms_pattern || !ms_stream || layer_bytes < (1u << 20) || layer_bytes % 16 || layers < 1 ||
+      layers > 1024 || steps < 1 || steps > 1000 || tail_blocks < 1 || tail_blocks > 65535)
+    return SKV_ERR_ARG;
+  return skv::dev_probe_launch_pattern(src, layer_bytes, layers, steps, tail_blocks, stream, ms_pattern, ms_stream);
+}
+
 }  // extern "C"

@@ -75,6 +75,8 @@ EXPORTS = {
     "skv_last_error": (ctypes.c_char_p, [_P]),
     "skv_probe_stream_read": (_I, [_P, ctypes.c_uint64, _I, _P, ctypes.POINTER(ctypes.c_double)]),
     "skv_probe_mfma_bf16": (_I, [_P, ctypes.POINTER(ctypes.c_double)]),
+    "skv_probe_launch_pattern": (_I, [_P, ctypes.c_uint64, _I, _I, _I, _P, ctypes.POINTER(ctypes.c_double),
+                                      ctypes.POINTER(ctypes.c_double)]),
 }
 
 _LIBS = {}
@@ -389,3 +391,24 @@ def skv_probe_mfma_bf16(stream=None) -> float:
         raise RuntimeError(f"skv_probe_mfma_bf16 failed: {_CODES.get(rc, rc)}")
     return out.value
 
+
+def skv_probe_launch_pattern(buf, layer_bytes: int, layers: int, steps: int = 20, tail_blocks: int = 128,
+                             stream=None, kind: str = "gpu"):
+    """(ms per step with a small dependent launch after every layer's streaming
+    read, ms per step of the streaming reads alone) over `layers` consecutive
+    layer_bytes slices of a device buffer (a CUDA tensor, or a raw address
+    with kind="host" for argument checks)."""
+    lib = load_library(kind)
+    if isinstance(buf, int):
+        addr, nbytes = buf, layer_bytes * layers
+    else:
+        addr, nbytes = buf.data_ptr(), buf.numel() * buf.element_size()
+    if layer_bytes * layers > nbytes:
+        raise SkvError(-1, "buffer smaller than layers * layer_bytes")
+    pat, st = ctypes.c_double(), ctypes.c_double()
+    rc = lib.skv_probe_launch_pattern(ctypes.c_void_p(addr), int(layer_bytes), int(layers), int(steps),
+                                      int(tail_blocks), _stream_handle(stream) if kind == "gpu" else None,
+                                      ctypes.byref(pat), ctypes.byref(st))
+    if rc != 0:
+        raise SkvError(rc, "skv_probe_launch_pattern failed")
+    return pat.value, st.value
