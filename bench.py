@@ -468,6 +468,14 @@ def main():
     stream_gbs = B.skv_probe_stream_read(probe_buf, reps=5)
     del probe_buf
     mfma_tflops = B.skv_probe_mfma_bf16()
+    # the same MFMA loop on normal draws as operands: the power limit sets the
+    # clock of a sustained matrix load, and real operand data draws more power
+    # than the constant operands above
+    og = torch.Generator(device=dev)
+    og.manual_seed(1004)
+    operands = torch.randn(8192, generator=og, device=dev).to(torch.bfloat16)  # 16 KiB
+    mfma_data_tflops = B.skv_probe_mfma_bf16_data(operands)
+    del operands
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats(dev)
 
@@ -639,6 +647,8 @@ def main():
         prefill = {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                    "frac": round(tf / BF16_PEAK_TFLOPS, 4), "kernel": f"prefill_kernel<{d},{(r + 15) // 16},2,8,false>",
                    "measured_peak": round(mfma_tflops, 1), "frac_of_measured": round(tf / mfma_tflops, 4),
+                   "measured_peak_data": round(mfma_data_tflops, 1),
+                   "frac_of_measured_data": round(tf / mfma_data_tflops, 4),
                    "flops_per_launch": fl, "avg_launch_ms": round(pms / pn, 4),
                    "ms_all_layers": round(pms, 3), "n_q_per_agent": prefill_n,
                    "view": base0 + Ssuf}

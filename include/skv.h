@@ -340,6 +340,12 @@ const char* skv_last_error(const skv_ctx* ctx);
  * skv_probe_mfma_bf16: a dense v_mfma_f32_16x16x32_bf16 issue loop, two waves
  *   per SIMD on every CU with independent accumulators; *tflops = the
  *   achieved dense bf16 rate (10^12 flop/s, 2 flops per multiply-add).
+ * skv_probe_mfma_bf16_data: the same issue loop on operand data: every wave
+ *   takes its eight A and eight B fragments from the first 16 KiB of the
+ *   device buffer src (bytes >= 16 KiB; caller-owned, e.g. normal draws in
+ *   bf16), so consecutive MFMAs see different bit patterns as attention's
+ *   do; runs about 10 ms per repetition so that the clock settles under the
+ *   power limit; *tflops = the best of three.
  * skv_probe_launch_pattern: the launch pattern of a decode step without its
  *   arithmetic. src holds `layers` consecutive buffers of layer_bytes bytes
  *   (a multiple of 16, at least 1 MiB; caller-owned, contents irrelevant).
@@ -354,6 +360,7 @@ const char* skv_last_error(const skv_ctx* ctx);
  * Errors: ARG (NULL pointers, bad sizes), HIP, UNSUPPORTED (CPU-only build). */
 int skv_probe_stream_read(const void* src, uint64_t bytes, int reps, void* stream, double* gbs);
 int skv_probe_mfma_bf16(void* stream, double* tflops);
+int skv_probe_mfma_bf16_data(const void* src, uint64_t bytes, void* stream, double* tflops);
 int skv_probe_launch_pattern(const void* src, uint64_t layer_bytes, int layers, int steps, int tail_blocks,
                              void* stream, double* ms_pattern, double* ms_stream);
 

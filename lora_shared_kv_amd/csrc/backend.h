@@ -106,9 +106,10 @@ int dev_set_timing(Geometry& g, int mask);
 int dev_collect_timing(Geometry& g, skv_kernel_times* out);
 const char* dev_last_error();
 // measurement probes (no context): see skv_probe_stream_read / skv_probe_mfma_bf16 /
-// skv_probe_launch_pattern
+// skv_probe_mfma_bf16_data / skv_probe_launch_pattern
 int dev_probe_stream_read(const void* src, uint64_t bytes, int reps, void* stream, double* gbs);
 int dev_probe_mfma_bf16(void* stream, double* tflops);
+int dev_probe_mfma_bf16_data(const void* src, void* stream, double* tflops);
 int dev_probe_launch_pattern(const void* src, uint64_t layer_bytes, int layers, int steps, int tail_blocks,
                              void* stream, double* ms_pattern, double* ms_stream);
 

@@ -50,6 +50,7 @@ int dev_collect_timing(Geometry&, skv_kernel_times* out) {
 const char* dev_last_error() { return ""; }
 int dev_probe_stream_read(const void*, uint64_t, int, void*, double*) { return SKV_ERR_UNSUPPORTED; }
 int dev_probe_mfma_bf16(void*, double*) { return SKV_ERR_UNSUPPORTED; }
+int dev_probe_mfma_bf16_data(const void*, void*, double*) { return SKV_ERR_UNSUPPORTED; }
 int dev_probe_launch_pattern(const void*, uint64_t, int, int, int, void*, double*, double*) {
   return SKV_ERR_UNSUPPORTED;
 }

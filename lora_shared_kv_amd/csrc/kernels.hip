@@ -2312,6 +2312,32 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters) {
   if (t[0] + t[1] + t[2] + t[3] == 1234.5f) skv::probe_sink[threadIdx.x & 3] = __float_as_uint(t[0]);
 }
 
+// The same issue loop on operand data: each wave takes eight A and eight B
+// fragments (16 bytes a lane each) from src, so consecutive MFMAs see
+// different bit patterns, as the operands of attention do. The matrix pipe's
+// power draw depends on them, and under a sustained load the power limit sets
+// the clock: constant operands run faster than real data.
+__global__ __launch_bounds__(256) void probe_mfma_data_kernel(const u32x4* __restrict__ src, int iters) {
+  const uint32_t lane = threadIdx.x & 63;
+  bf16x8 a[8], b[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    a[j] = __builtin_bit_cast(bf16x8, src[j * 64 + lane]);
+    b[j] = __builtin_bit_cast(bf16x8, src[(8 + j) * 64 + lane]);
+  }
+  f32x4 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0, 0, 0, 0};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = mfma(a[j], b[j], acc[j]);
+  }
+  f32x4 t = acc[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) t += acc[j];
+  if (t[0] + t[1] + t[2] + t[3] == 1234.5f) skv::probe_sink[threadIdx.x & 3] = __float_as_uint(t[0]);
+}
+
 // The launch-pattern probe's pair: a one-workgroup-per-CU streaming read of a
 // layer-sized buffer that leaves one word per wave, then a small launch of
 // single-row workgroups that reads those words (so it is ordered after the
@@ -2899,6 +2925,20 @@ int dev_probe_launch_pattern(const void* src, uint64_t layer_bytes, int layers, 
   }
   *ms_pattern = pat;
   *ms_stream = str;
+  return SKV_OK;
+}
+
+int dev_probe_mfma_bf16_data(const void* src, void* stream, double* tflops) {
+  // long enough (about 10 ms) for the clock to settle under the power limit
+  constexpr int kIters = 65536, kBlocks = 2 * kCUs;  // two waves per SIMD
+  const double ms = probe_best_ms((hipStream_t)stream, 3, dim3(kBlocks), probe_mfma_data_kernel,
+                                  (const u32x4*)src, kIters);
+  if (ms <= 0) {
+    set_err("probe_mfma_data_kernel", hipGetLastError());
+    return SKV_ERR_HIP;
+  }
+  const double flops = (double)kBlocks * 4 * kIters * 8 * (16.0 * 16 * 32 * 2);
+  *tflops = flops / (ms * 1e-3) / 1e12;
   return SKV_OK;
 }
 

@@ -899,6 +899,11 @@ int skv_probe_mfma_bf16(void* stream, double* tflops) {
   return skv::dev_probe_mfma_bf16(stream, tflops);
 }
 
+int skv_probe_mfma_bf16_data(const void* src, uint64_t bytes, void* stream, double* tflops) {
+  if (!src || !tflops || bytes < (16u << 10)) return SKV_ERR_ARG;
+  return skv::dev_probe_mfma_bf16_data(src, stream, tflops);
+}
+
 int skv_probe_launch_pattern(const void* src, uint64_t layer_bytes, int layers, int steps, int tail_blocks,
                              void* stream, double* ms_pattern, double* ms_stream) {
   if (!src || !ms_pattern || !ms_stream || layer_bytes < (1u << 20) || layer_bytes % 16 || layers < 1 ||

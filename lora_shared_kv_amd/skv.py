@@ -75,6 +75,7 @@ EXPORTS = {
     "skv_last_error": (ctypes.c_char_p, [_P]),
     "skv_probe_stream_read": (_I, [_P, ctypes.c_uint64, _I, _P, ctypes.POINTER(ctypes.c_double)]),
     "skv_probe_mfma_bf16": (_I, [_P, ctypes.POINTER(ctypes.c_double)]),
+    "skv_probe_mfma_bf16_data": (_I, [_P, ctypes.c_uint64, _P, ctypes.POINTER(ctypes.c_double)]),
     "skv_probe_launch_pattern": (_I, [_P, ctypes.c_uint64, _I, _I, _I, _P, ctypes.POINTER(ctypes.c_double),
                                       ctypes.POINTER(ctypes.c_double)]),
 }
@@ -389,6 +390,23 @@ def skv_probe_mfma_bf16(stream=None) -> float:
     rc = lib.skv_probe_mfma_bf16(_stream_handle(stream), ctypes.byref(out))
     if rc != 0:
         raise RuntimeError(f"skv_probe_mfma_bf16 failed: {_CODES.get(rc, rc)}")
+    return out.value
+
+
+def skv_probe_mfma_bf16_data(buf, stream=None, kind: str = "gpu") -> float:
+    """Dense bf16 MFMA rate (TFLOP/s) of the issue loop on operand data taken
+    from a device buffer (a CUDA tensor of at least 16 KiB, or a raw address
+    with kind="host" for argument checks)."""
+    lib = load_library(kind)
+    if isinstance(buf, int):
+        addr, nbytes = buf, 16 << 10
+    else:
+        addr, nbytes = buf.data_ptr(), buf.numel() * buf.element_size()
+    out = ctypes.c_double()
+    rc = lib.skv_probe_mfma_bf16_data(ctypes.c_void_p(addr), int(nbytes),
+                                      _stream_handle(stream) if kind == "gpu" else None, ctypes.byref(out))
+    if rc != 0:
+        raise SkvError(rc, "skv_probe_mfma_bf16_data failed")
     return out.value
 
 

@@ -20,6 +20,24 @@ def test_mfma_probe(torch_cuda):
 
 
 @pytest.mark.gpu
+def test_mfma_probe_on_operand_data(torch_cuda):
+    g = torch_cuda.Generator(device="cuda")
+    g.manual_seed(7)
+    operands = torch_cuda.randn(8192, generator=g, device="cuda").to(torch_cuda.bfloat16)
+    tflops = B.skv_probe_mfma_bf16_data(operands)
+    assert 100.0 < tflops < 3000.0, tflops
+
+
+def test_mfma_data_probe_checks_arguments():
+    with pytest.raises(B.SkvError) as e:
+        B.skv_probe_mfma_bf16_data(0, kind="host")
+    assert e.value.code == "ARG"
+    with pytest.raises(B.SkvError) as e:
+        B.skv_probe_mfma_bf16_data(1 << 40, kind="host")
+    assert e.value.code == "UNSUPPORTED"
+
+
+@pytest.mark.gpu
 def test_probe_rejects_bad_sizes(torch_cuda):
     buf = torch_cuda.empty(1 << 16, dtype=torch_cuda.uint8, device="cuda")
     with pytest.raises(RuntimeError):
