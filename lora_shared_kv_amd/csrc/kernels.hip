@@ -106,6 +106,18 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return r;
 }
 
+// s_waitcnt WAIT, then a bare s_barrier; no LDS access moves across either.
+template <int WAIT>
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(WAIT);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// s_waitcnt for every LDS and scalar-memory operation alone (vector-memory
+// and export counters at their maxima)
+constexpr int kWaitLdsOnly = 15 | (7 << 4) | (3 << 14);
+
 // Zero the first nm of the eight bf16 values of x (value 2k is the low half
 // of 32-bit word k). nm <= 0 keeps all of them, nm >= 8 zeroes all.
 __device__ __forceinline__ bf16x8 zero_leading(bf16x8 x, int nm) {
@@ -680,27 +692,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     s_ckey[c] = (seg << 24) | key0;
   }
 
-  // per-lane query rows: Q^T B-operand slices, agent and base length of the row
-  bf16x8 qf[RB][KS];
-  int row_agent[RB], row_b[RB], row_S[RB], row_lrb[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int rho = rb * 16 + n;
-    const int a = rho / p.G;
-    const bool ok = rho < p.R;
-    row_agent[rb] = ok ? a : -1;
-    row_b[rb] = ok ? p.ag_b[a] : 0;
-    row_S[rb] = ok ? p.ag_S[a] : 0;
-    row_lrb[rb] = ok ? p.ag_lrb[a] : 0;
-    const u16* qp = p.q + ((uint64_t)a * p.Hq + g * p.G + rho % p.G) * D;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qf[rb][s] = ok ? ld8(qp + 32 * s + 8 * q) : zero8();
-  }
   // Low-rank A-operand row of this lane in block mb: stacked row sr = 16mb + n
   // is rank sr % r of plane sr / r. For an own-suffix chunk the other agents'
   // planes hold don't-care rows: their products only reach rows that are
   // masked out for that chunk, or stacked entries a row never keeps. A lane
-  // past the last plane reads a valid row and masks it to zero.
+  // past the last plane reads a valid row and masks it to zero. Set up before
+  // the query loads: the first chunk loads need these addresses, and the wait
+  // for them must not include the query loads.
   uint32_t lr_mask[MB];
   const u16* lr_row[MB];
 #pragma unroll
@@ -710,6 +708,30 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     const bool ok = pi < p.n_planes;
     lr_mask[mb] = ok ? 0xffffffffu : 0u;
     lr_row[mb] = p.LRT + (uint64_t)p.planes[ok ? pi : 0] * p.lr_plane + (ok ? k : 0) * kPage;
+  }
+  // per-lane query rows: Q^T B-operand slices, agent and base length of the row
+  bf16x8 qf[RB][KS];
+  int row_agent[RB], row_b[RB], row_S[RB], row_lrb[RB];
+  // Every load here is unconditional (a padding lane reads agent 0's row and
+  // drops it): loads under a divergent condition would leave the compiler's
+  // count of loads in flight unknown at the join, and the first chunk loads
+  // would then wait for all of them.
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int rho = rb * 16 + n;
+    const bool ok = rho < p.R;
+    const int a = ok ? rho / p.G : 0;
+    const int b_a = p.ag_b[a], S_a = p.ag_S[a], lrb_a = p.ag_lrb[a];
+    row_agent[rb] = ok ? a : -1;
+    row_b[rb] = ok ? b_a : 0;
+    row_S[rb] = ok ? S_a : 0;
+    row_lrb[rb] = ok ? lrb_a : 0;
+    const u16* qp = p.q + ((uint64_t)a * p.Hq + g * p.G + (ok ? rho % p.G : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8 v = ld8(qp + 32 * s + 8 * q);
+      qf[rb][s] = ok ? v : zero8();
+    }
   }
 
   float m_run[RB], l_run[RB];
@@ -723,7 +745,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) lacc[rb][mb] = f32x4{0, 0, 0, 0};
   }
-  __syncthreads();
+  // the chunk table is in LDS; the query loads stay in flight (a full
+  // workgroup fence here would hold the first chunk loads behind them)
+  stage_barrier<kWaitLdsOnly>();
 
   const uint64_t head_off = (uint64_t)g * kPage * D;  // offset of head g inside a page
   const uint64_t page_elems = (uint64_t)p.Hkv * kPage * D;
@@ -1993,14 +2017,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // others end at once, and a barrier waits only for waves that have not ended).
 constexpr int kWideRows = 128;  // tokens per tile of the wide form
 
-// s_waitcnt WAIT, then a bare s_barrier; no LDS access moves across either.
-template <int WAIT>
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(WAIT);
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 template <int D, int NS, int NH>
 __global__ __launch_bounds__(64 * (2 * NH + 4)) void project_wide_kernel(ProjectParams p) {
   static_assert(NH == 3 || NH == 4, "three or four half units per tile");
