@@ -64,6 +64,9 @@ struct AttnAgent {
 struct AttnJob {
   int layer;
   int n;
+  // First page id when the shared pages every view of the job reads are one
+  // run of consecutive ids (shared page i is shared_run + i), else -1.
+  int32_t shared_run = -1;
   AttnAgent ag[SKV_MAX_AGENTS];
   const uint16_t* q;  // [sum n_q][Hq][D]
   const uint16_t* B;  // [N][r][Hkv*D]

@@ -647,6 +647,7 @@ struct DecodeParams {
   int planes[SKV_MAX_AGENTS];     // stacked low-rank planes of this group
   int seg_off[SKV_MAX_AGENTS + 1];  // flattened offset of each own suffix; seg_off[n] = total
   int shared_len;                 // flattened length of the shared segment (max_b padded)
+  int shared_run;                 // first id of the shared pages when they are consecutive, else -1
   int head_chunks;     // C: 32-key chunks of one head's flattened sequence
   int items_per_head;  // I: item j takes chunks [j C / I, (j + 1) C / I)
   float scale_log2;
@@ -677,7 +678,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
   const int f0 = 32 * c_lo;
   const int n_ck = c_hi - c_lo;
 
-  // chunk descriptors: segment (0 = shared, 1 + a = agent a's suffix), first key, page
+  // chunk descriptors: segment (0 = shared, 1 + a = agent a's suffix), first key,
+  // page. Shared pages whose ids run consecutively need no table read, which
+  // would otherwise sit in front of the item's first chunk loads.
   for (int c = threadIdx.x; c < n_ck; c += blockDim.x) {
     const int fc = f0 + 32 * c;
     int seg = 0, key0 = fc;
@@ -687,8 +690,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
       seg = 1 + a;
       key0 = fc - p.seg_off[a];
     }
-    const int32_t* table = p.tbl + (seg == 0 ? 0 : 1 + p.ag_id[seg - 1]) * p.tbl_seq;
-    s_cpage[c] = table[key0 / kPage];
+    int page;
+    if (seg == 0 && p.shared_run >= 0) {
+      page = p.shared_run + key0 / kPage;
+    } else {
+      const int32_t* table = p.tbl + (seg == 0 ? 0 : 1 + p.ag_id[seg - 1]) * p.tbl_seq;
+      page = table[key0 / kPage];
+    }
+    s_cpage[c] = page;
     s_ckey[c] = (seg << 24) | key0;
   }
 
@@ -2776,6 +2785,7 @@ static int decode_impl(const Geometry& g, const AttnJob& job, const AppendJob* a
     // flattened key sequence per KV head: shared prefix, then each own suffix,
     // each padded to whole 32-key chunks
     p.shared_len = (max_b + 31) / 32 * 32;
+    p.shared_run = job.shared_run;
     p.seg_off[0] = p.shared_len;
     for (int i = 0; i < n; ++i) p.seg_off[i + 1] = p.seg_off[i] + (p.ag_S[i] + 31) / 32 * 32;
     const int chunks = p.seg_off[n] / 32;

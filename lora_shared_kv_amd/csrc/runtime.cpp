@@ -514,6 +514,19 @@ int skv_append_agents(skv_ctx* c, int layer, int n, const int* agents, const int
   return finish_agent_rows(c, layer, n, agents, counts, total, x != nullptr, ar, rc);
 }
 
+// The first id of the shared pages the job's views read, when they are one
+// run of consecutive ids, else -1 (the decode then looks each page up).
+static int32_t shared_run(const skv_ctx* c, const Layer& l, const AttnJob& job) {
+  int max_b = 0;
+  for (int i = 0; i < job.n; ++i) max_b = std::max(max_b, (int)job.ag[i].b);
+  const int pages = ceil_div(max_b, c->g.ps);
+  const std::vector<int32_t>& t = l.tbl[0];
+  if (pages == 0 || (int)t.size() < pages) return -1;
+  for (int i = 1; i < pages; ++i)
+    if (t[i] != t[0] + i) return -1;
+  return t[0];
+}
+
 static int validate_attend(skv_ctx* c, int layer, int n, const int* agents, const int* base_len,
                            const int* suffix_len, const int* n_q, const void* q, const void* B,
                            const void* o, AttnJob& job) {
@@ -553,6 +566,7 @@ static int validate_attend(skv_ctx* c, int layer, int n, const int* agents, cons
   job.q = (const uint16_t*)q;
   job.B = (const uint16_t*)B;
   job.o = (uint16_t*)o;
+  job.shared_run = shared_run(c, l, job);
   return SKV_OK;
 }
 
@@ -627,6 +641,7 @@ static int decode_step(skv_ctx* c, int layer, int n, const int* agents, const in
     job.ag[i] = skv::AttnAgent{a, b, S, p, 1, i, c->lr_begin[a]};
     need += ceil_div(S + 1, g.ps) - (int)l.tbl[1 + a].size();
   }
+  job.shared_run = shared_run(c, l, job);
   if (need > (int)l.free.size())
     return c->fail(SKV_ERR_OOM, "layer %d: %d pages needed, %d free", layer, need, (int)l.free.size());
   char msg[256];

@@ -622,6 +622,39 @@ def test_agent_ops_never_touch_shared_pages():
     assert B.skv_get_pages(gpu.ctx, 0, -1) == sp
 
 
+@pytest.mark.parametrize("shape_name", ["llama3", "qwen3"])
+def test_decode_over_scattered_shared_pages(shape_name):
+    # The shared prefix grows after the agents took pages of their own, so its
+    # page ids no longer run consecutively and the decode looks each shared
+    # page up in the table; the agents attach at different lengths (one view
+    # inside the first, consecutive run of pages, one past it), then decode
+    # and the fused step run against the oracle.
+    from lora_shared_kv_amd import skv as B
+    R = _runner()
+    shape = synth.WORKLOADS[shape_name].with_(n_agents=2)
+    sc = Schedule(shape, 41, n_layers=1)
+    sc.draw_adapters()
+    sc.shared_prefix(150)
+    sc.attach(0, 150)
+    sc.attach(1, 150)
+    sc.own_rows(0, [0, 1], [70, 70])
+    sc.shared_prefix(330)
+    sc.attach(0, 100)   # drops its own rows; view inside the first, consecutive pages
+    sc.attach(1, 150)   # drops its own rows ...
+    sc.attach(1, 480)   # ... and attaches past them
+    sc.own_rows(0, [0, 1], [5, 9])
+    sc.attend("prefill", 0, [0, 1], [5, 9], tag="prefill")
+    for t in range(3):
+        sc.own_rows(0, [0, 1], [1, 1])
+        sc.attend("decode", 0, [0, 1], [1, 1], tag=f"decode{t}")
+    for t in range(3):
+        sc.decode_step(0, [0, 1], tag=f"step{t}")
+    gpu, _, res = R.run_parity(sc, max_pages=64, log=log)
+    shared = B.skv_get_pages(gpu.ctx, 0, -1)
+    assert any(shared[i + 1] != shared[i] + 1 for i in range(len(shared) - 1)), shared
+    assert len(res) == 7
+
+
 def test_length_mismatch_is_rejected_without_launch():
     import torch
     from lora_shared_kv_amd import skv as B
