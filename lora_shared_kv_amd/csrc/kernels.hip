@@ -655,12 +655,20 @@ struct DecodeParams {
   AppendParams app;
 };
 
+// LDS slots of wave state the split pass's fold uses: one per wave where they
+// fit (one fold stage), else two (pairwise folds).
+template <int D, int RB, int MB>
+constexpr int split_fold_slots() {
+  constexpr int slot = RB * ((D / 16 + MB) * 64 * 16 + 2 * 64 * 4);
+  return 4 * slot <= 128 * 1024 ? 4 : 2;
+}
+
 template <int D, int RB, int MB>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
   constexpr int KS = D / 32, DB = D / 16;
   __shared__ int32_t s_cpage[kMaxItemChunks];   // page id of each chunk of the item
   __shared__ int32_t s_ckey[kMaxItemChunks];    // (segment << 24) | first key of the chunk in its segment
-  extern __shared__ __attribute__((aligned(16))) float s_buf[];  // [4 or 2][RB*16][W]
+  extern __shared__ __attribute__((aligned(16))) float s_buf[];  // the waves' states (fold), or append staging
 
   if ((int)blockIdx.x < p.n_app) {
     // fused decode step: write the new low-rank rows and page-table entries;
@@ -869,15 +877,21 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     }
   }
 
-  // Fold the four waves' states pairwise through LDS (waves 2 and 3 into 0 and
-  // 1, then 1 into 0), each lane exchanging exactly the accumulator quads it
-  // holds, so the slots are read and written conflict-free in MFMA layout.
-  // Wave 0 then writes the item's partial rows (o, o_lr, m, l) for the merge.
+  // Fold the four waves' states through LDS and write the item's partial rows
+  // (o, o_lr, m, l) for the merge. Each lane exchanges exactly the accumulator
+  // quads it holds (MFMA layout), so slots are written and read conflict-free.
+  //  - one stage, where a slot per wave fits in LDS: every wave puts its state,
+  //    then wave w combines quads w, w + 4, ... of the four slots, each slot
+  //    weighted by 2^(m_s - M) with M the largest of the slots' maxima, and
+  //    stores them; wave 0 also writes each row's m and l;
+  //  - else pairwise (waves 2 and 3 into 0 and 1, then 1 into 0), and wave 0
+  //    writes the rows.
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) l_run[rb] = xsum16_32(l_run[rb]);
   constexpr int NQ = DB + MB;  // accumulator quads per lane and row block
-  f32x4* const s_st = reinterpret_cast<f32x4*>(s_buf);                  // [2][RB][NQ][64]
-  float* const s_ml = reinterpret_cast<float*>(s_st + 2 * RB * NQ * 64);  // [2][RB][2][64]
+  constexpr int NS = split_fold_slots<D, RB, MB>();
+  f32x4* const s_st = reinterpret_cast<f32x4*>(s_buf);                   // [NS][RB][NQ][64]
+  float* const s_ml = reinterpret_cast<float*>(s_st + NS * RB * NQ * 64);  // [NS][RB][2][64]
   auto put = [&](int slot) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -890,50 +904,90 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
       s_ml[((slot * RB + rb) * 2 + 1) * 64 + lane] = l_run[rb];
     }
   };
-  auto fold = [&](int slot) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const f32x4* const st = s_st + (slot * RB + rb) * NQ * 64 + lane;
-      const float mo = s_ml[((slot * RB + rb) * 2) * 64 + lane];
-      const float lo = s_ml[((slot * RB + rb) * 2 + 1) * 64 + lane];
-      const float mc = fmaxf(m_run[rb], mo);
-      const float a = __builtin_amdgcn_exp2f(m_run[rb] - mc), b = __builtin_amdgcn_exp2f(mo - mc);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[rb][db] = oacc[rb][db] * a + st[db * 64] * b;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) lacc[rb][mb] = lacc[rb][mb] * a + st[(DB + mb) * 64] * b;
-      l_run[rb] = l_run[rb] * a + lo * b;
-      m_run[rb] = mc;
-    }
-  };
-  if (w >= 2) put(w - 2);
-  __syncthreads();
-  if (w < 2) fold(w);
-  if (w == 1) put(1);
-  __syncthreads();
-  if (w != 0) return;
-  fold(1);
   const int W = p.W;
   float* const dst = p.part + (uint64_t)item * p.R * W;
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int rho = rb * 16 + n;
-    if (rho >= p.R) continue;
-    float* const row = dst + rho * W;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(row + db * 16 + 4 * q) = oacc[rb][db];
-    // keep the stacked low-rank entries of the row's own plane
+  // the stacked low-rank entries of quad j (j >= DB) that belong to the row's own plane
+  auto put_lr = [&](float* row, int rho, int j, const f32x4& v) {
     const int pidx = p.ag_pidx[rho / p.G];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int jj = 0; jj < 4; ++jj) {
+      const int sr = (j - DB) * 16 + 4 * q + jj;
+      if (sr / p.r == pidx) row[D + sr % p.r] = v[jj];
+    }
+  };
+  if constexpr (NS == 4) {
+    put(w);
+    __syncthreads();
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int sr = mb * 16 + 4 * q + jj;
-        if (sr / p.r == pidx) row[D + sr % p.r] = lacc[rb][mb][jj];
+    for (int rb = 0; rb < RB; ++rb) {
+      const int rho = rb * 16 + n;
+      float ms[4], ws[4];
+      float M = -INFINITY;
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        ms[sl] = s_ml[((sl * RB + rb) * 2) * 64 + lane];
+        M = fmaxf(M, ms[sl]);
       }
-    if (q == 0) {
-      row[D + p.r] = m_run[rb];
-      row[D + p.r + 1] = l_run[rb];
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) ws[sl] = __builtin_amdgcn_exp2f(ms[sl] - M);
+      if (rho >= p.R) continue;
+      float* const row = dst + rho * W;
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) {
+        if ((j & 3) != w) continue;
+        f32x4 acc = s_st[rb * NQ * 64 + j * 64 + lane] * ws[0];
+#pragma unroll
+        for (int sl = 1; sl < 4; ++sl) acc += s_st[(sl * RB + rb) * NQ * 64 + j * 64 + lane] * ws[sl];
+        if (j < DB)
+          *reinterpret_cast<f32x4*>(row + j * 16 + 4 * q) = acc;
+        else
+          put_lr(row, rho, j, acc);
+      }
+      if (w == 0 && q == 0) {
+        float l = 0.f;
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) l += s_ml[((sl * RB + rb) * 2 + 1) * 64 + lane] * ws[sl];
+        row[D + p.r] = M;
+        row[D + p.r + 1] = l;
+      }
+    }
+  } else {
+    auto fold = [&](int slot) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const f32x4* const st = s_st + (slot * RB + rb) * NQ * 64 + lane;
+        const float mo = s_ml[((slot * RB + rb) * 2) * 64 + lane];
+        const float lo = s_ml[((slot * RB + rb) * 2 + 1) * 64 + lane];
+        const float mc = fmaxf(m_run[rb], mo);
+        const float a = __builtin_amdgcn_exp2f(m_run[rb] - mc), b = __builtin_amdgcn_exp2f(mo - mc);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[rb][db] = oacc[rb][db] * a + st[db * 64] * b;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) lacc[rb][mb] = lacc[rb][mb] * a + st[(DB + mb) * 64] * b;
+        l_run[rb] = l_run[rb] * a + lo * b;
+        m_run[rb] = mc;
+      }
+    };
+    if (w >= 2) put(w - 2);
+    __syncthreads();
+    if (w < 2) fold(w);
+    if (w == 1) put(1);
+    __syncthreads();
+    if (w != 0) return;
+    fold(1);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int rho = rb * 16 + n;
+      if (rho >= p.R) continue;
+      float* const row = dst + rho * W;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(row + db * 16 + 4 * q) = oacc[rb][db];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) put_lr(row, rho, DB + mb, lacc[rb][mb]);
+      if (q == 0) {
+        row[D + p.r] = m_run[rb];
+        row[D + p.r + 1] = l_run[rb];
+      }
     }
   }
 }
@@ -2452,7 +2506,7 @@ int w_of(const skv::Geometry& g) { return g.D + g.r + 4; }
 template <int D, int RB, int MB>
 int launch_split_t(const skv::Geometry& g, const DecodeParams& p, int items, bool timed) {
   constexpr int DB = D / 16, NQ = DB + MB;
-  size_t lds = (size_t)2 * RB * (NQ * 64 * 16 + 2 * 64 * 4);          // two slots of wave states
+  size_t lds = (size_t)split_fold_slots<D, RB, MB>() * RB * (NQ * 64 * 16 + 2 * 64 * 4);  // wave states
   if (p.n_app > 0) lds = std::max(lds, (size_t)64 * (128 + 8) * 2);  // append blocks' staging
   return launch(g, timed ? 2 : -1, decode_split_kernel<D, RB, MB>, dim3(p.n_app + items), lds, p,
                 "decode_split_kernel");
