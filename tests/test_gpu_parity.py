@@ -655,6 +655,31 @@ def test_decode_over_scattered_shared_pages(shape_name):
     assert len(res) == 7
 
 
+def test_maximum_sizes():
+    # The plan's largest cases on a small head shape (8 KV heads of 64):
+    #  - a prefill over a view of exactly 4,096 pages (262,144 keys, the page
+    #    list a prefill workgroup holds in LDS), 64 queries at its end;
+    #  - fused decode steps over a 520,000-key shared prefix: 16,250 chunks per
+    #    KV head need 32 items per head at up to 508 chunks each (the chunk
+    #    table's cap is 512), which with the step's two append blocks is more
+    #    workgroups than CUs.
+    R = _runner()
+    shape = Shape("max", 1, 8, 8, 64, 128, 8, 2, BASE_SHARED, 0)
+    view = 4096 * 64
+    sc = Schedule(shape, 77, n_layers=1)
+    sc.draw_adapters()
+    sc.shared_prefix(520_000)
+    sc.attach(0, view - 64)
+    sc.attach(1, 520_000)
+    sc.own_rows(0, [0], [64])
+    sc.attend("prefill", 0, [0], [64], tag="prefill at the view limit")
+    # per KV head: 16,250 shared chunks + agent 0's 3 own (65-66 rows) + agent 1's 1;
+    # (256 CUs - 2 append blocks) / 8 heads = 31 items would need 525 chunks each
+    for t in range(2):
+        sc.decode_step(0, [0, 1], tag=f"step{t}")
+    R.run_parity(sc, max_pages=520_000 // 64 + 16, log=log)
+
+
 def test_length_mismatch_is_rejected_without_launch():
     import torch
     from lora_shared_kv_amd import skv as B
