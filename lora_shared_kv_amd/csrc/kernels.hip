@@ -522,7 +522,9 @@ __device__ void append_lr_mfma_block(const AppendParams& p, int s, int tile, cha
 // 64-column sections per slab of the MFMA low-rank tiles at ranks up to 16
 // (2 for kernels with a tight register budget, whose dot-product rows then
 // take rank 32 in two passes).
-template <bool KV = true, bool MFMA_LR = true, int NTA = 256, int HS = 4>
+// KV / LR: compile the K/V copies / the low-rank rows (a launch whose jobs
+// never carry one leaves its code, and its registers, out).
+template <bool KV = true, bool MFMA_LR = true, int NTA = 256, int HS = 4, bool LR = true>
 __device__ void append_block(const AppendParams& p, int b, char* smem) {
   static_assert(!MFMA_LR || NTA == 256, "the MFMA low-rank tiles are written for four waves");
   if (b == 0 && p.update_tables) {
@@ -542,6 +544,7 @@ __device__ void append_block(const AppendParams& p, int b, char* smem) {
     }
     return;
   }
+  if constexpr (!LR) return;
   b -= n_kv;
   int s = 0;
   while (b >= p.lr_block0[s + 1]) ++s;
@@ -769,11 +772,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
   const uint64_t head_off = (uint64_t)g * kPage * D;  // offset of head g inside a page
   const uint64_t page_elems = (uint64_t)p.Hkv * kPage * D;
 
-  // Two 32-key chunk buffers per wave: the loop is unrolled by two so the
-  // buffers never need copying, and every prefetch is unconditional (the tail
-  // is peeled), so the compiler keeps the next chunk's loads in flight while
-  // the current chunk is consumed. K and V^T are streamed once, so their
-  // loads are non-temporal.
+  // Two 32-key chunk buffers per wave (one for 64 query rows, below): the loop
+  // is unrolled by two so the buffers never need copying, and every prefetch
+  // is unconditional (the tail is peeled), so the compiler keeps the next
+  // chunk's loads in flight while the current chunk is consumed. K and V^T are
+  // streamed once, so their loads are non-temporal.
   struct Chunk {
     bf16x8 k[2][KS], v[DB];
     u32x4 l[MB];  // raw low-rank rows; the lane mask is applied where they are used
@@ -854,7 +857,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     }
   };
   const int n_chunks = w < n_ck ? (n_ck - w + 3) / 4 : 0;  // this wave's chunks: w, w + 4, ...
-  if (n_chunks > 0) {
+  if constexpr (RB >= 4) {
+    // 64 query rows: their accumulators leave no registers for a second chunk
+    // buffer, so each chunk is loaded, then used
+    Chunk A;
+    for (int i = 0; i < n_chunks; ++i) {
+      load(w + 4 * i, A);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(w + 4 * i, A);
+    }
+  } else if (n_chunks > 0) {
     Chunk A, Bf;
     load(w, A);
     int i = 0;
@@ -1040,7 +1052,7 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(MergeParams p) {
   if ((int)blockIdx.x >= p.n_rows) {
     // fused decode step: copy the new K/V rows into the pages; the rows merged
     // here take the new token from the step's inputs instead
-    append_block<true, false, NT>(p.app, blockIdx.x - p.n_rows, s_app);
+    append_block<true, false, NT, 4, false>(p.app, blockIdx.x - p.n_rows, s_app);
     return;
   }
   __shared__ float s_w[kMaxMergeSlots];
