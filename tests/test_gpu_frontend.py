@@ -143,6 +143,10 @@ ODD_UNITS = Shape("odd-units-d64", 1, 3, 1, 64, 256, 8, 2, BASE_SHARED, 0)
 WIDE_D64 = Shape("wide-d64", 1, 64, 16, 64, 256, 8, 2, BASE_SHARED, 0)
 # the llama3 heads with hidden 960: an odd number (15) of 64-column stages
 ODD_STAGES = Shape("odd-stages", 1, 32, 8, 128, 960, 8, 4, BASE_LR_SHARED, 0)
+# the largest packed weights the front end takes: (64 + 2 x 64) x 128 features x
+# 43,648 columns x 2 bytes = 2,145,386,496 bytes, 2^18 below 2 GiB (32-bit byte
+# offsets into the weights run up to there)
+MAX_WEIGHTS = Shape("max-weights", 1, 64, 64, 128, 43648, 8, 2, BASE_SHARED, 0)
 
 
 @pytest.mark.parametrize("name,shape,prefix,own,counts,theta", [
@@ -259,3 +263,9 @@ def test_project_append_odd_stage_count(counts):
     # 15 stages of 64 hidden columns: the split form's quarters differ in
     # length, and the wide and tall forms end on an odd stage
     run_case(ODD_STAGES, 64, [0, 0, 0, 0], counts, 500000.0, seed=21, attend=False)
+
+
+@pytest.mark.parametrize("counts", [[3, 3], [300, 0]], ids=["split", "wide"])
+def test_project_append_largest_weights(counts):
+    assert (64 + 2 * 64) * 128 * 43648 * 2 == 2_145_386_496 < 1 << 31
+    run_case(MAX_WEIGHTS, 64, [0, 0], counts, 10000.0, seed=22, attend=False)
