@@ -225,6 +225,10 @@ EDGE = [
     ("8agents-R32", Shape("e", 1, 16, 4, 128, 256, 16, 8, BASE_SHARED, 0), 500, [3] * 8, {}),
     ("16agents-R64-BLS", Shape("e", 1, 16, 4, 64, 256, 8, 16, BASE_LR_SHARED, 0), 257, [2] * 16, {}),
     ("16agents-BS-groups", Shape("e", 1, 8, 2, 64, 128, 16, 16, BASE_SHARED, 0), 190, [1] * 16, {}),
+    # 64 stacked rows at head dim 128 (one buffered chunk per wave, pairwise fold), ranks 8 and 32
+    ("16agents-R64-BLS-d128", Shape("e", 1, 16, 4, 128, 256, 8, 16, BASE_LR_SHARED, 0), 700, [2] * 16, {}),
+    ("16agents-R64-BLS-d128-r32", Shape("e", 1, 16, 4, 128, 256, 32, 16, BASE_LR_SHARED, 0), 333,
+     [1, 0] * 8, {}),
     ("peaked-logits", Shape("e", 1, 8, 2, 128, 256, 16, 2, BASE_SHARED, 0), 1500, [100, 7],
      dict(peaked=4.0)),
     ("zero-lr-prefix", Shape("e", 1, 8, 2, 128, 256, 16, 2, BASE_SHARED, 0), 640, [33, 3],
