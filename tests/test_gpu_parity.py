@@ -229,6 +229,14 @@ EDGE = [
     ("16agents-R64-BLS-d128", Shape("e", 1, 16, 4, 128, 256, 8, 16, BASE_LR_SHARED, 0), 700, [2] * 16, {}),
     ("16agents-R64-BLS-d128-r32", Shape("e", 1, 16, 4, 128, 256, 32, 16, BASE_LR_SHARED, 0), 333,
      [1, 0] * 8, {}),
+    # the remaining split-pass tile shapes (head dim, 16-row blocks, 16-rank blocks):
+    # (64, 1, 8) eight planes of rank 16; (128, 2, 4) and (64, 2, 4) four planes over 32 rows;
+    # (64, 2, 2) two planes over 32 rows; (64, 4, 2) rank 32 over 64 rows
+    ("tiles-d64-1x8", Shape("e", 1, 4, 2, 64, 128, 16, 8, BASE_SHARED, 0), 300, [1, 0, 2, 0, 3, 0, 4, 0], {}),
+    ("tiles-d128-2x4", Shape("e", 1, 16, 2, 128, 256, 16, 4, BASE_SHARED, 0), 260, [5, 0, 1, 3], {}),
+    ("tiles-d64-2x4", Shape("e", 1, 8, 1, 64, 128, 16, 4, BASE_SHARED, 0), 190, [0, 2, 7, 1], {}),
+    ("tiles-d64-2x2", Shape("e", 1, 16, 1, 64, 128, 16, 2, BASE_SHARED, 0), 450, [9, 2], {}),
+    ("tiles-d64-4x2", Shape("e", 1, 16, 4, 64, 128, 32, 16, BASE_LR_SHARED, 0), 129, [1] * 16, {}),
     ("peaked-logits", Shape("e", 1, 8, 2, 128, 256, 16, 2, BASE_SHARED, 0), 1500, [100, 7],
      dict(peaked=4.0)),
     ("zero-lr-prefix", Shape("e", 1, 8, 2, 128, 256, 16, 2, BASE_SHARED, 0), 640, [33, 3],
@@ -263,14 +271,21 @@ def test_private_prefix_layout(shape_name):
     assert len(res) == 4
 
 
-@pytest.mark.parametrize("shape_name", ["llama3", "qwen3"])
+# rank 32 (two 16-rank blocks in the prefill and decode tiles) at head dims 64 and 128
+OFFSET_SHAPES = {
+    "d64-r32-BLS": Shape("d64-r32", 1, 8, 2, 64, 256, 32, 3, BASE_LR_SHARED, 0),
+    "d128-r32-BS": Shape("d128-r32", 1, 8, 4, 128, 256, 32, 2, BASE_SHARED, 0),
+}
+
+
+@pytest.mark.parametrize("shape_name", ["llama3", "qwen3", "d64-r32-BLS", "d128-r32-BS"])
 def test_activation_offsets(shape_name):
     """Adapter activation offsets (RoleKV, "What it does": the adapter switches
     on after the role's header): 0, inside the shared prefix, inside the own
     suffix and beyond the view, through prefill, fused decode steps and a plain
     decode; the last agent's new tokens lie before its offset."""
     R = _runner()
-    shape = synth.WORKLOADS[shape_name]
+    shape = OFFSET_SHAPES.get(shape_name) or synth.WORKLOADS[shape_name]
     N = shape.n_agents
     prefix, own = 4096, 256
     sc = synth.Schedule(shape, 1012, n_layers=1)
