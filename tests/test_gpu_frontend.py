@@ -161,6 +161,8 @@ MAX_WEIGHTS = Shape("max-weights", 1, 64, 64, 128, 43648, 8, 2, BASE_SHARED, 0)
     ("qwen3-takeover", QWEN3_HEADS, 160, [0, 0], [200, 64], 1000000.0),
     # head dim 64: one unit per head, a last workgroup with idle waves
     ("tiny-d64", TINY_HEADS, 1024, [0, 0], [100, 37], 10000.0),
+    # head dim 64 in the split form
+    ("tiny-d64-split", TINY_HEADS, 1024, [2, 0], [3, 4], 10000.0),
 ])
 def test_project_append_matches_oracle(name, shape, prefix, own, counts, theta):
     run_case(shape, prefix, own, counts, theta, seed=11)

@@ -271,14 +271,16 @@ def test_private_prefix_layout(shape_name):
     assert len(res) == 4
 
 
-# rank 32 (two 16-rank blocks in the prefill and decode tiles) at head dims 64 and 128
+# head dim 64 at rank 8, and rank 32 (two 16-rank blocks in the prefill and decode tiles) at head dims 64
+# and 128
 OFFSET_SHAPES = {
+    "d64-r8-BS": Shape("d64-r8", 1, 14, 2, 64, 896, 8, 2, BASE_SHARED, 0),
     "d64-r32-BLS": Shape("d64-r32", 1, 8, 2, 64, 256, 32, 3, BASE_LR_SHARED, 0),
     "d128-r32-BS": Shape("d128-r32", 1, 8, 4, 128, 256, 32, 2, BASE_SHARED, 0),
 }
 
 
-@pytest.mark.parametrize("shape_name", ["llama3", "qwen3", "d64-r32-BLS", "d128-r32-BS"])
+@pytest.mark.parametrize("shape_name", ["llama3", "qwen3", "d64-r8-BS", "d64-r32-BLS", "d128-r32-BS"])
 def test_activation_offsets(shape_name):
     """Adapter activation offsets (RoleKV, "What it does": the adapter switches
     on after the role's header): 0, inside the shared prefix, inside the own
