@@ -701,6 +701,60 @@ def test_maximum_sizes():
     R.run_parity(sc, max_pages=520_000 // 64 + 16, log=log)
 
 
+RANDOM_SHAPES = [
+    Shape("rnd-d64-BS", 1, 8, 2, 64, 128, 8, 3, BASE_SHARED, 0),
+    Shape("rnd-d128-BLS", 1, 8, 4, 128, 256, 16, 2, BASE_LR_SHARED, 0),
+    Shape("rnd-d64-G4-BS", 1, 4, 1, 64, 128, 4, 4, BASE_SHARED, 0),
+    Shape("rnd-d128-r32-BLS", 1, 16, 2, 128, 256, 32, 2, BASE_LR_SHARED, 0),
+]
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_random_schedules(seed):
+    # Seeded random interleavings of every operation on one store: own-row
+    # appends, suffix prefills, decodes, fused decode steps, crops (inside the
+    # suffix, into the shared prefix, then a re-attach) and activation offsets,
+    # over lengths that start and end anywhere in a page; every attention call
+    # is checked against the oracle.
+    rng = np.random.RandomState(seed)
+    R = _runner()
+    shape = RANDOM_SHAPES[seed % len(RANDOM_SHAPES)]
+    N = shape.n_agents
+    sc = Schedule(shape, 3000 + seed, n_layers=1)
+    sc.draw_adapters()
+    P = int(rng.randint(0, 700))
+    if P:
+        sc.shared_prefix(P, lr="x" if rng.rand() < 0.7 else "zero")
+    for a in range(N):
+        sc.attach(a, int(rng.randint(0, P + 1)))
+    view = lambda a: sc.b[a] + sc.S[0][a]
+    subset = lambda: [a for a in range(N) if rng.rand() < 0.6] or [int(rng.randint(N))]
+    for t in range(14):
+        op = rng.choice(["own", "prefill", "decode", "step", "crop", "offset"], p=[.2, .2, .15, .25, .1, .1])
+        if op == "own":
+            ag = subset()
+            sc.own_rows(0, ag, [int(rng.randint(1, 81)) for _ in ag])
+        elif op == "prefill":
+            ag = [a for a in subset() if view(a) > 0]
+            if ag:
+                sc.attend("prefill", 0, ag, [int(rng.randint(1, min(view(a), 48) + 1)) for a in ag], tag=f"prefill{t}")
+        elif op == "decode":
+            ag = subset()
+            sc.own_rows(0, ag, [1] * len(ag))
+            sc.attend("decode", 0, ag, [1] * len(ag), tag=f"decode{t}")
+        elif op == "step":
+            sc.decode_step(0, subset(), lr="x" if rng.rand() < 0.8 else "zero", tag=f"step{t}")
+        elif op == "crop":
+            a = int(rng.randint(N))
+            sc.crop(a, int(rng.randint(0, view(a) + 1)))
+            if sc.S[0][a] == 0 and rng.rand() < 0.5:
+                sc.attach(a, int(rng.randint(sc.b[a], P + 1)))
+        else:
+            a = int(rng.randint(N))
+            sc.set_lr_begin(a, int(rng.randint(0, view(a) + 50)))
+    R.run_parity(sc, max_pages=256, log=lambda m: log(f"[seed {seed}] {m}"))
+
+
 def test_length_mismatch_is_rejected_without_launch():
     import torch
     from lora_shared_kv_amd import skv as B
