@@ -421,7 +421,7 @@ def main():
                     help="also run a plain 1 GiB device copy (for counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus}).",
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 
