@@ -1201,7 +1201,8 @@ struct PrefillParams {
 };
 
 // LDS image of one page of one KV head: the K tile and the V^T tile (64 x D
-// each, in operand order) and the page's low-rank rows (r x 64).
+// each, in operand order) and the page's low-rank rows (up to 32 ranks x 64
+// keys, in operand order).
 template <int D>
 constexpr int prefill_page_elems() { return 2 * 64 * D + 32 * 64; }
 
@@ -1218,6 +1219,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_rsrc(const void* base, in
 __device__ __forceinline__ void dma_block(__amdgpu_buffer_rsrc_t r, int off, u16* dst_wave, int lane) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)dst_wave, 16, off + lane * 16,
                                            0, 0, 0);
+}
+// The same with each lane's own source offset (a gather into the wave's
+// contiguous 1 KB of LDS).
+__device__ __forceinline__ void dma_lanes(__amdgpu_buffer_rsrc_t r, int off_lane, u16* dst_wave) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)dst_wave, 16, off_lane, 0, 0,
+                                           0);
 }
 
 // LDS (address space 3) views of the page ring: 32-bit addresses, so a read's
@@ -1297,7 +1304,6 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
     for (int s = 0; s < KS; ++s) qf[rb][s] = ok ? ld8(qp + 32 * s + 8 * q) : zero8();
   }
   const u16* lrb = p.LRT + (uint64_t)p.ag_plane[ai] * p.lr_plane;
-  const int lr_blocks = (p.r * 64 * 2 + 1023) / 1024;  // 1 KB blocks of a page's low-rank rows
   // lowest view position among the wave's valid rows: a key at or below it is
   // visible to all of them
   int tmin = 0x7fffffff;
@@ -1324,11 +1330,17 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
     const uint32_t one = ones_row && mb * 16 + n == p.r ? 0x3f803f80u : 0u;
     lr_ones[mb] = u32x4{one, one, one, one};
   }
-  // this lane's low-rank operand row of block mb in a page buffer: rank
-  // 16 mb + n (lanes past the last rank read the last one; masked above)
+  // A page's low-rank rows sit in LDS in operand order, RP = 16 MB ranks
+  // (the ranks past r hold zeros): 16-byte slot h 4RP + q RP + k holds rank k,
+  // keys 32h + 8q .. 32h + 8q + 7, so the sixteen lanes of one q read
+  // consecutive slots. (Rank rows 128 bytes apart, as in the cache, put eight
+  // ranks on two groups of banks.) This lane's operand of block mb: rank
+  // 16 mb + n (lanes past the last rank read the last one; masked above),
+  // half h at a constant 4RP slots further.
+  constexpr int RP = 16 * MB;
   int lr_elems[MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) lr_elems[mb] = 2 * 64 * D + min(mb * 16 + n, p.r - 1) * kPage + 8 * q;
+  for (int mb = 0; mb < MB; ++mb) lr_elems[mb] = 2 * 64 * D + 8 * (q * RP + min(mb * 16 + n, p.r - 1));
   auto lr_lane = [&](int mb, int buf) { return lane_ptr(buf, lr_elems[mb]); };
 
   // With LRO (some agent has an adapter activation offset), the low-rank rows
@@ -1364,15 +1376,23 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
   const uint64_t page_elems = (uint64_t)p.Hkv * kPage * D;
   // Page copies into LDS are issued by the first wave group (waves [0, NW/2)):
   // each of its waves moves KC of the K tile's 1 KB blocks, as many of the
-  // V^T tile's, and the low-rank block w (waves past the page's block count
-  // repeat block 0, the same bytes to the same place). With r = 4 the second
-  // half of that block lies past the page's rows and lands as zeros; it is
-  // never read.
+  // V^T tile's, and the low-rank block w (waves past the block count repeat
+  // block 0, the same bytes to the same place). A low-rank block is 64 slots
+  // of the operand order above: each lane fetches the 16 bytes of its slot
+  // from the page's rank rows (offset k 128 + 64 h + 16 q); ranks past r lie
+  // past the page's rows and land as zeros.
   constexpr int NG = NW / 2;       // waves per group
   constexpr int KC = D / 8 / NG;   // 1 KB blocks of a K (or V^T) tile per copying wave
   static_assert(KC * NG * 8 == D, "page tile blocks must split evenly over a wave group");
   constexpr int NC = 2 * KC + 1;   // copies one copying wave issues per page
+  constexpr int lr_blocks = RP / 8;  // 1 KB blocks of the low-rank slots
+  static_assert(lr_blocks <= NG, "one low-rank block per copying wave");
   const int lb = w < lr_blocks ? w : 0;
+  int lr_src;  // this lane's source offset in the page's low-rank rows
+  {
+    const int sl = 64 * lb + lane, hh = sl / (4 * RP), rem = sl % (4 * RP);
+    lr_src = (rem % RP) * 128 + 64 * hh + 16 * (rem / RP);
+  }
   struct PageSrc {
     __amdgpu_buffer_rsrc_t k, v, l;
   };
@@ -1389,7 +1409,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
       const int blk = w * KC + c - KC;
       dma_block(src.v, blk * 1024, dst + 64 * D + blk * 512, lane);
     } else {
-      dma_block(src.l, lb * 1024, dst + 2 * 64 * D + lb * 512, lane);
+      dma_lanes(src.l, lr_src, dst + 2 * 64 * D + lb * 512);
     }
   };
   auto copy_page = [&](int page, int buf) {
@@ -1445,7 +1465,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const u32x4 raw = __builtin_bit_cast(u32x4, *reinterpret_cast<lds_frag*>(lr_lane(mb, (j - 1) % 3) + h * 32));
+          const u32x4 raw =
+              __builtin_bit_cast(u32x4, *reinterpret_cast<lds_frag*>(lr_lane(mb, (j - 1) % 3) + h * 32 * RP));
           const u32x4 keep = LRO ? lr_keep(j - 1, h) : u32x4{~0u, ~0u, ~0u, ~0u};
           const bf16x8 lf = __builtin_bit_cast(bf16x8, (raw & lr_mask[mb] & keep) | lr_ones[mb]);
 #pragma unroll
@@ -1493,7 +1514,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
       return *reinterpret_cast<lds_frag*>(kvp + 64 * D + f * 512);
     if (f < NV + NL) {  // low-rank rows: block mb, half h
       const int mb = (f - NV) >> 1, h = (f - NV) & 1;
-      return *reinterpret_cast<lds_frag*>(kvl[mb] + h * 32);
+      return *reinterpret_cast<lds_frag*>(kvl[mb] + h * 32 * RP);
     }
     // K tile (ht, s), taken chunk-major (s outer) so that consecutive MFMAs
     // update different score tiles
